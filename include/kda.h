@@ -1,0 +1,183 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) hot path.
+ *
+ * What is computed.  Per (sequence, head) a fixed d_k x d_v fp32 state S is carried
+ * through the tokens.  Each token t applies a per-channel decay and then a
+ * beta-weighted erase-and-write, and reads the output from the updated state:
+ *
+ *     gt_t = min(0, max(-5, g_t))                 per key channel (floor at -5)
+ *     S'   = Diag(exp(gt_t)) S                    decay the key rows of S
+ *     u_t  = beta_t (v_t - S'^T k_t)              erase what S' recalls for k_t
+ *     S    = S' + k_t u_t^T                       write
+ *     o_t  = S^T q_t                              read after the write
+ *
+ * and optionally  out_t = o_t / sqrt(mean_j o_tj^2 + eps) * w * sigmoid(gate_t).
+ *
+ * Sources (web pages on Kimi K3; none prints the formulas, see the design notes for
+ * the readings taken):
+ *   [R] "xhh.club" tag page 结构, entry on KDA's recurrent form: per-channel decay and
+ *       erase-and-write into a 128x128 per-head state independent of context length;
+ *       per-head RMSNorm and a full-rank sigmoid output gate.
+ *   [C] same page, entry on the chunkwise-parallel algorithm: chunks linked by a
+ *       state recurrence and computed inside with matrix products; the -5 floor on
+ *       each step's log-decay lets the 16-token diagonal tiles run as BF16 matmul;
+ *       training/prefill use the chunkwise form, decode the recurrent form.
+ *   [S] same page, entry on the structure's system implications: three execution
+ *       forms (fast kernel, intra-device context parallelism, state rollback);
+ *       context parallelism decomposes by an associative prefix scan, never by
+ *       adding states; the prefix cache reuses state at 512-token boundaries.
+ *   [G] "nlpx.cn" Kimi K3 reading guide, section 6: KCP passes segment transitions;
+ *       why the floor is -5 and why the reciprocal cumulative decay overflows
+ *       without it; why per-rank states cannot be summed; why the prefix cache
+ *       needs KDA checkpoints.
+ *
+ * Conventions for every entry point.
+ *   - All data pointers are DEVICE pointers on the current HIP device, owned by
+ *     the caller.  The library allocates nothing and keeps no pointer after
+ *     returning.
+ *   - Layouts are dense row-major: activations token-major [B, T, H, d], states
+ *     [B, H, d_k, d_v] (row = key channel, column = value channel).
+ *   - Argument errors are reported synchronously and nothing is launched.  Work
+ *     is enqueued asynchronously on `stream`; faults surface at the caller's
+ *     synchronisation.  A launch failure returns KDA_ERR_HIP.  No C++ exception
+ *     crosses this boundary.
+ *   - Only gfx950 devices are supported (KDA_ERR_DEVICE otherwise).
+ *   - Calls are thread-safe; calls that share output buffers must be ordered by
+ *     the caller.
+ *   - Supported shapes: d_k = d_v = 128.
+ *   - NaN/Inf in inputs propagate; the library does not scrub them.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+#if defined(__GNUC__) || defined(__clang__)
+#define KDA_API __attribute__((visibility("default")))
+#else
+#define KDA_API
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,         /* a required pointer is NULL */
+  KDA_ERR_SHAPE = 2,        /* a size is negative or inconsistent */
+  KDA_ERR_UNSUPPORTED = 3,  /* valid but not implemented (d != 128, chunk, dtype) */
+  KDA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required */
+  KDA_ERR_ALIAS = 5,        /* an output overlaps an input it must not overlap */
+  KDA_ERR_DEVICE = 6,       /* current device is not gfx950 or cannot be queried */
+  KDA_ERR_HIP = 7           /* a HIP launch failed */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/*
+ * Chunkwise prefill ([C]; the chunkwise form is the prefill form).  Processes T
+ * tokens of B independent sequences and H heads from state S0, writing o for
+ * every token and the final state.
+ *
+ * Numerics.  in_dtype = KDA_BF16: the 16-token diagonal tiles of the intra-chunk
+ * products run as BF16 MFMA (operands split into bf16 high and low parts), the
+ * remaining products as fp16 MFMA, all with fp32 accumulation; the state is kept
+ * in fp32.  The fp16 operands are the v values, the state copy and quantities
+ * bounded by |q|, |k|, |v| and |S|: they must stay below 65504 in magnitude.
+ * in_dtype = KDA_F32: every product runs as fp32 MFMA.
+ */
+typedef struct kda_prefill_desc {
+  int32_t B, T, H;          /* T >= 0; any T (a ragged last chunk is handled) */
+  int32_t d_k, d_v;         /* must be 128 */
+  int32_t chunk;            /* 16 or 64 tokens per chunk */
+  int32_t in_dtype;         /* kda_dtype of q, k, v and gate */
+  int32_t out_dtype;        /* kda_dtype of o */
+  const void *q;            /* [B,T,H,d_k] */
+  const void *k;            /* [B,T,H,d_k] */
+  const void *v;            /* [B,T,H,d_v] */
+  const float *g;           /* [B,T,H,d_k] per-channel log-decay; clamped to [-5, 0] */
+  const float *beta;        /* [B,T,H] write strength, used as given */
+  const float *S0;          /* [B,H,d_k,d_v] initial state, or NULL for zeros */
+  float *S_final;           /* [B,H,d_k,d_v] final state, or NULL; may equal S0 */
+  void *o;                  /* [B,T,H,d_v]; must not overlap any input */
+  const void *gate;         /* [B,T,H,d_v] gate logits, or NULL: then o is raw S^T q */
+  const float *norm_weight; /* [d_v] RMSNorm weight, or NULL for ones (gate only) */
+  float norm_eps;           /* RMSNorm epsilon (gate only), e.g. 1e-6 */
+  int32_t ckpt_every;       /* 0, or a multiple of chunk: checkpoint period in tokens */
+  float *ckpt;              /* [B, T/ckpt_every, H, d_k, d_v]: state after the first
+                               m*ckpt_every tokens, m = 1..T/ckpt_every ([S]: 512) */
+  int32_t n_segments;       /* 0 = choose; 1 = one pass; >1 = split every sequence into
+                               that many segments combined by an associative scan of
+                               their state maps ([S], [G]) */
+  int32_t v_split;          /* 0 = choose; else 1, 2 or 4 workgroups per (seq, head)
+                               splitting the d_v columns of the state */
+  void *workspace;          /* device scratch of kda_prefill_workspace_size() bytes */
+  size_t workspace_bytes;
+} kda_prefill_desc;
+
+/* Bytes of workspace kda_prefill_chunked needs for this descriptor (pointers are
+ * not read).  Returns the same argument errors as kda_prefill_chunked. */
+KDA_API kda_status kda_prefill_workspace_size(const kda_prefill_desc *d, size_t *bytes);
+
+/* Enqueue the prefill.  Errors: NULL (q/k/v/g/beta/o, or ckpt when ckpt_every > 0,
+ * or workspace when one is needed), SHAPE (negative sizes, ckpt_every not a
+ * multiple of chunk, n_segments > number of chunks), UNSUPPORTED (d != 128, chunk
+ * not 16/64, bad dtype, v_split not 0/1/2/4), WORKSPACE, ALIAS (o overlapping an
+ * input, or S_final overlapping an input other than S0), DEVICE, HIP. */
+KDA_API kda_status kda_prefill_chunked(const kda_prefill_desc *d, hipStream_t stream);
+
+/*
+ * One recurrent decode step ([C]: decode uses the recurrent form; [R]) for N
+ * independent sequences and H heads: every state is read and written once, in
+ * place.  fp32 arithmetic throughout.
+ */
+typedef struct kda_decode_desc {
+  int32_t N, H;             /* N >= 0 sequences */
+  int32_t d_k, d_v;         /* must be 128 */
+  int32_t in_dtype;         /* kda_dtype of q, k, v and gate */
+  int32_t out_dtype;        /* kda_dtype of o */
+  const void *q;            /* [N,H,d_k] */
+  const void *k;            /* [N,H,d_k] */
+  const void *v;            /* [N,H,d_v] */
+  const float *g;           /* [N,H,d_k] log-decay; clamped to [-5, 0] */
+  const float *beta;        /* [N,H] */
+  float *state;             /* [N,H,d_k,d_v] fp32, updated in place */
+  void *o;                  /* [N,H,d_v]; must not overlap any input or the state */
+  const void *gate;         /* [N,H,d_v] or NULL (then o is raw S^T q) */
+  const float *norm_weight; /* [d_v] or NULL */
+  float norm_eps;
+} kda_decode_desc;
+
+/* Errors: NULL, SHAPE, UNSUPPORTED, ALIAS, DEVICE, HIP as for the prefill. */
+KDA_API kda_status kda_decode_step(const kda_decode_desc *d, hipStream_t stream);
+
+/*
+ * State checkpoint and rollback ([S]: state rollback is one of KDA's execution
+ * forms; the prefix cache keeps checkpoints).  Both copy n_states fp32 states of
+ * d_k x d_v on the stream: checkpoint ckpt[i] = state[i], rollback
+ * state[i] = ckpt[i].  The two buffers must not overlap (KDA_ERR_ALIAS).
+ * n_states = 0 is a no-op.  Errors: NULL, SHAPE (n_states < 0, d_k or d_v < 1),
+ * ALIAS, DEVICE, HIP.
+ */
+KDA_API kda_status kda_state_checkpoint(const float *state, float *ckpt, int64_t n_states, int32_t d_k,
+                                int32_t d_v, hipStream_t stream);
+KDA_API kda_status kda_state_rollback(float *state, const float *ckpt, int64_t n_states, int32_t d_k,
+                              int32_t d_v, hipStream_t stream);
+
+/* Static, NUL-terminated description of a status code. */
+KDA_API const char *kda_status_string(kda_status s);
+
+/* KDA_ABI_VERSION of the built library. */
+KDA_API int32_t kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -31,7 +31,7 @@ import numpy as np
 __all__ = [
     "F32", "BF16", "f32_to_bf16", "bf16_to_f32", "to_f64",
     "PrefillCase", "DecodeStep", "WORKLOADS", "make_prefill", "make_workload", "make_decode_state",
-    "make_decode_step", "workload",
+    "make_decode_step", "make_decode_steps", "workload",
 ]
 
 F32 = "f32"
@@ -303,3 +303,28 @@ def make_decode_step(N: int, H: int, d: int = 128, *, seed: int = 0, step: int =
     g = np.maximum(-5.0, _logsigmoid(nrm(_G, (N, H, d), loc=2.0))).astype(np.float32)
     beta = _sigmoid(nrm(_BETA, (N, H))).astype(np.float32)
     return DecodeStep(N, H, d, in_dtype, q, k, v, g, beta)
+
+
+def make_decode_steps(N: int, H: int, d: int = 128, *, seed: int = 0, steps: int = 1,
+                      first_step: int = 0, in_dtype: str = BF16, threads: int | None = None):
+    """Token inputs of `steps` consecutive decode steps, stacked on a leading axis:
+    returns dict q, k, v [S,N,H,d], g [S,N,H,d], beta [S,N,H].  Step s uses the same
+    draws as make_decode_step(step=first_step + s)."""
+    dt = np.uint16 if in_dtype == BF16 else np.float32
+    out = dict(q=np.empty((steps, N, H, d), dt), k=np.empty((steps, N, H, d), dt),
+               v=np.empty((steps, N, H, d), dt), g=np.empty((steps, N, H, d), np.float32),
+               beta=np.empty((steps, N, H), np.float32))
+
+    def work(s):
+        st = make_decode_step(N, H, d, seed=seed, step=first_step + s, in_dtype=in_dtype)
+        out["q"][s], out["k"][s], out["v"][s], out["g"][s], out["beta"][s] = \
+            st.q, st.k, st.v, st.g, st.beta
+
+    nt = threads or _threads()
+    if nt > 1 and steps > 1:
+        with _fut.ThreadPoolExecutor(nt) as ex:
+            list(ex.map(work, range(steps)))
+    else:
+        for s in range(steps):
+            work(s)
+    return out

@@ -1,0 +1,205 @@
+"""ctypes binding of libkda.so (include/kda.h): argument marshalling only.
+
+Each function has the name of the C entry point it calls, takes torch tensors that
+live on the current HIP device, fills the C descriptor and raises KdaError on a
+non-zero status.  Every step of the computation runs in the HIP kernels; torch only
+provides device memory and the stream.  There is no fallback: if the library is
+missing or the device is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkda.so")
+
+KDA_OK, KDA_ERR_NULL, KDA_ERR_SHAPE, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, \
+    KDA_ERR_ALIAS, KDA_ERR_DEVICE, KDA_ERR_HIP = range(8)
+KDA_F32, KDA_BF16 = 0, 1
+
+_DT = {torch.float32: KDA_F32, torch.bfloat16: KDA_BF16}
+
+
+class KdaError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn}: status {status}: {msg}")
+        self.status = status
+
+
+class PrefillDesc(C.Structure):
+    _fields_ = [
+        ("B", C.c_int32), ("T", C.c_int32), ("H", C.c_int32),
+        ("d_k", C.c_int32), ("d_v", C.c_int32), ("chunk", C.c_int32),
+        ("in_dtype", C.c_int32), ("out_dtype", C.c_int32),
+        ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
+        ("g", C.c_void_p), ("beta", C.c_void_p), ("S0", C.c_void_p),
+        ("S_final", C.c_void_p), ("o", C.c_void_p), ("gate", C.c_void_p),
+        ("norm_weight", C.c_void_p), ("norm_eps", C.c_float),
+        ("ckpt_every", C.c_int32), ("ckpt", C.c_void_p),
+        ("n_segments", C.c_int32), ("v_split", C.c_int32),
+        ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+    ]
+
+
+class DecodeDesc(C.Structure):
+    _fields_ = [
+        ("N", C.c_int32), ("H", C.c_int32), ("d_k", C.c_int32), ("d_v", C.c_int32),
+        ("in_dtype", C.c_int32), ("out_dtype", C.c_int32),
+        ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
+        ("g", C.c_void_p), ("beta", C.c_void_p), ("state", C.c_void_p), ("o", C.c_void_p),
+        ("gate", C.c_void_p), ("norm_weight", C.c_void_p), ("norm_eps", C.c_float),
+    ]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libkda.so (raises OSError if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise OSError(f"{path} not found: build it with "
+                          "`python -m linear_attention_sequence_kda_amd.build`")
+        lib = C.CDLL(path)
+        vp = C.c_void_p
+        lib.kda_prefill_workspace_size.argtypes = [C.POINTER(PrefillDesc), C.POINTER(C.c_size_t)]
+        lib.kda_prefill_workspace_size.restype = C.c_int
+        lib.kda_prefill_chunked.argtypes = [C.POINTER(PrefillDesc), vp]
+        lib.kda_prefill_chunked.restype = C.c_int
+        lib.kda_decode_step.argtypes = [C.POINTER(DecodeDesc), vp]
+        lib.kda_decode_step.restype = C.c_int
+        lib.kda_state_checkpoint.argtypes = [vp, vp, C.c_int64, C.c_int32, C.c_int32, vp]
+        lib.kda_state_checkpoint.restype = C.c_int
+        lib.kda_state_rollback.argtypes = [vp, vp, C.c_int64, C.c_int32, C.c_int32, vp]
+        lib.kda_state_rollback.restype = C.c_int
+        lib.kda_status_string.argtypes = [C.c_int]
+        lib.kda_status_string.restype = C.c_char_p
+        lib.kda_abi_version.argtypes = []
+        lib.kda_abi_version.restype = C.c_int32
+        _lib = lib
+    return _lib
+
+
+def status_string(st: int) -> str:
+    return load().kda_status_string(st).decode()
+
+
+def _check(fn: str, st: int) -> None:
+    if st != KDA_OK:
+        raise KdaError(fn, st, status_string(st))
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("tensor must be on the HIP device")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _dtype(t) -> int:
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise ValueError(f"unsupported dtype {t.dtype}; use float32 or bfloat16") from None
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else stream
+
+
+def kda_abi_version() -> int:
+    return int(load().kda_abi_version())
+
+
+def _prefill_desc(q, k, v, g, beta, *, o, S0=None, S_final=None, gate=None, norm_weight=None,
+                  norm_eps=1e-6, chunk=64, ckpt_every=0, ckpt=None, n_segments=0, v_split=0,
+                  workspace=None) -> PrefillDesc:
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    d = PrefillDesc()
+    d.B, d.T, d.H, d.d_k, d.d_v, d.chunk = B, T, H, dk, dv, chunk
+    d.in_dtype = _dtype(q)
+    d.out_dtype = _dtype(o) if o is not None else KDA_F32
+    d.q, d.k, d.v, d.g, d.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    d.S0, d.S_final, d.o, d.gate = _ptr(S0), _ptr(S_final), _ptr(o), _ptr(gate)
+    d.norm_weight, d.norm_eps = _ptr(norm_weight), float(norm_eps)
+    d.ckpt_every, d.ckpt = int(ckpt_every), _ptr(ckpt)
+    d.n_segments, d.v_split = int(n_segments), int(v_split)
+    if workspace is not None:
+        d.workspace, d.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    return d
+
+
+def kda_prefill_workspace_size(q, k, v, g, beta, **kw) -> int:
+    """Workspace bytes kda_prefill_chunked needs for these arguments."""
+    kw.setdefault("o", None)
+    d = _prefill_desc(q, k, v, g, beta, **kw)
+    n = C.c_size_t(0)
+    _check("kda_prefill_workspace_size", load().kda_prefill_workspace_size(C.byref(d), C.byref(n)))
+    return int(n.value)
+
+
+def kda_prefill_chunked(q, k, v, g, beta, *, o, S0=None, S_final=None, gate=None,
+                        norm_weight=None, norm_eps=1e-6, chunk=64, ckpt_every=0, ckpt=None,
+                        n_segments=0, v_split=0, workspace=None, stream=None) -> None:
+    """Chunkwise prefill into the caller's `o` (and S_final / ckpt when given).
+
+    q, k: [B,T,H,128]; v, gate: [B,T,H,128] (all float32 or all bfloat16); g: [B,T,H,128]
+    float32; beta: [B,T,H] float32; S0, S_final: [B,H,128,128] float32; o: [B,T,H,128]
+    float32 or bfloat16; ckpt: [B, T // ckpt_every, H, 128, 128] float32.  If the plan needs
+    a workspace and none is given, one is allocated from torch's caching allocator."""
+    kw = dict(o=o, S0=S0, S_final=S_final, gate=gate, norm_weight=norm_weight, norm_eps=norm_eps,
+              chunk=chunk, ckpt_every=ckpt_every, ckpt=ckpt, n_segments=n_segments,
+              v_split=v_split)
+    if workspace is None:
+        n = kda_prefill_workspace_size(q, k, v, g, beta, **kw)
+        if n > 0:
+            workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    d = _prefill_desc(q, k, v, g, beta, workspace=workspace, **kw)
+    _check("kda_prefill_chunked", load().kda_prefill_chunked(C.byref(d), _stream(stream)))
+
+
+def kda_decode_step(q, k, v, g, beta, state, *, o, gate=None, norm_weight=None, norm_eps=1e-6,
+                    stream=None) -> None:
+    """One decode step for [N,H,*] inputs; `state` [N,H,128,128] float32 is updated in place."""
+    N, H, dk = q.shape
+    d = DecodeDesc()
+    d.N, d.H, d.d_k, d.d_v = N, H, dk, v.shape[-1]
+    d.in_dtype, d.out_dtype = _dtype(q), _dtype(o)
+    d.q, d.k, d.v, d.g, d.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    d.state, d.o, d.gate = _ptr(state), _ptr(o), _ptr(gate)
+    d.norm_weight, d.norm_eps = _ptr(norm_weight), float(norm_eps)
+    _check("kda_decode_step", load().kda_decode_step(C.byref(d), _stream(stream)))
+
+
+def _n_states(t) -> int:
+    return t.numel() // (t.shape[-1] * t.shape[-2]) if t.dim() >= 2 else 0
+
+
+def kda_state_checkpoint(state, ckpt, *, stream=None) -> None:
+    """ckpt[...] = state[...] (fp32 states of shape [..., d_k, d_v])."""
+    if ckpt.shape != state.shape:
+        raise ValueError("state and checkpoint shapes differ")
+    _check("kda_state_checkpoint",
+           load().kda_state_checkpoint(_ptr(state), _ptr(ckpt), _n_states(state), state.shape[-2],
+                                       state.shape[-1], _stream(stream)))
+
+
+def kda_state_rollback(state, ckpt, *, stream=None) -> None:
+    """state[...] = ckpt[...] (fp32 states of shape [..., d_k, d_v])."""
+    if ckpt.shape != state.shape:
+        raise ValueError("state and checkpoint shapes differ")
+    _check("kda_state_rollback",
+           load().kda_state_rollback(_ptr(state), _ptr(ckpt), _n_states(state), state.shape[-2],
+                                     state.shape[-1], _stream(stream)))

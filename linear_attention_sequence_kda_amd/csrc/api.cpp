@@ -1,0 +1,254 @@
+// C ABI of the KDA library: argument validation, execution planning, dispatch.
+// Validation is synchronous and launches nothing on error; every launch is
+// asynchronous on the caller's stream.  No exception crosses the boundary.
+#include <hip/hip_runtime_api.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "internal.h"
+#include "kda.h"
+
+namespace {
+
+using kda::PrefillPlan;
+
+// ---------------------------------------------------------------------------
+// device check: gfx950 only, cached per device ordinal
+// ---------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+kda_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return KDA_ERR_DEVICE;
+  if (dev >= kMaxDevices) return KDA_ERR_DEVICE;
+  int st = g_dev_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return KDA_ERR_DEVICE;
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_dev_state[dev].store(st, std::memory_order_release);
+  }
+  return st == 1 ? KDA_OK : KDA_ERR_DEVICE;
+}
+
+// [p, p + n) and [q, q + m) overlap (empty ranges never overlap).
+bool overlap(const void *p, size_t n, const void *q, size_t m) {
+  if (!p || !q || n == 0 || m == 0) return false;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p), b = reinterpret_cast<uintptr_t>(q);
+  return a < b + m && b < a + n;
+}
+
+size_t esize(int32_t dt) { return dt == KDA_BF16 ? 2 : 4; }
+
+bool valid_dtype(int32_t dt) { return dt == KDA_F32 || dt == KDA_BF16; }
+
+// ---------------------------------------------------------------------------
+// prefill planning
+// ---------------------------------------------------------------------------
+constexpr int kTargetWorkgroups = 256;   // one per CU of MI355X
+
+kda_status plan_prefill(const kda_prefill_desc &d, PrefillPlan *p) {
+  std::memset(p, 0, sizeof(*p));
+  const int64_t n_chunks = d.T > 0 ? (static_cast<int64_t>(d.T) + d.chunk - 1) / d.chunk : 0;
+  const int64_t units = static_cast<int64_t>(d.B) * d.H;
+  p->n_chunks = static_cast<int>(n_chunks);
+
+  // columns per workgroup
+  int vs = d.v_split;
+  if (vs == 0) {
+    vs = 1;
+    while (vs < 4 && units * vs * 2 <= kTargetWorkgroups) vs *= 2;
+  }
+  p->v_split = vs;
+
+  // segments
+  int64_t ns = d.n_segments;
+  if (ns > 1 && ns > n_chunks) return KDA_ERR_SHAPE;
+  if (ns == 0) {
+    ns = 1;
+    // Split long sequences when (sequence, head, column slice) units cannot fill the chip
+    // and each segment still keeps >= 32 chunks.
+    while (units * vs * ns * 2 <= kTargetWorkgroups && n_chunks / (ns * 2) >= 32) ns *= 2;
+  }
+  if (ns < 1) ns = 1;
+  int64_t seg_chunks = n_chunks > 0 ? (n_chunks + ns - 1) / ns : 0;
+  if (seg_chunks > 0) ns = (n_chunks + seg_chunks - 1) / seg_chunks;  // no empty segments
+  p->n_seg = static_cast<int>(ns);
+  p->seg_chunks = static_cast<int>(seg_chunks);
+  p->split_norm = d.gate != nullptr && vs > 1;
+
+  const size_t dkdv = static_cast<size_t>(d.d_k) * d.d_v;
+  if (p->n_seg > 1) {
+    p->ws_maps = static_cast<size_t>(units) * p->n_seg * dkdv * 2 * sizeof(float);
+    p->ws_sin = static_cast<size_t>(units) * p->n_seg * dkdv * sizeof(float);
+  }
+  if (p->split_norm)
+    p->ws_norm = static_cast<size_t>(units) * static_cast<size_t>(d.T) * vs * sizeof(float);
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  p->ws_total = up(p->ws_maps) + up(p->ws_sin) + up(p->ws_norm);
+  return KDA_OK;
+}
+
+kda_status validate_sizes(const kda_prefill_desc *d) {
+  if (!d) return KDA_ERR_NULL;
+  if (d->B < 0 || d->T < 0 || d->H < 0) return KDA_ERR_SHAPE;
+  if (d->d_k != 128 || d->d_v != 128) return KDA_ERR_UNSUPPORTED;
+  if (d->chunk != 16 && d->chunk != 64) return KDA_ERR_UNSUPPORTED;
+  if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return KDA_ERR_UNSUPPORTED;
+  if (d->v_split != 0 && d->v_split != 1 && d->v_split != 2 && d->v_split != 4)
+    return KDA_ERR_UNSUPPORTED;
+  if (d->n_segments < 0) return KDA_ERR_SHAPE;
+  if (d->ckpt_every < 0 || (d->ckpt_every > 0 && d->ckpt_every % d->chunk != 0)) return KDA_ERR_SHAPE;
+  return KDA_OK;
+}
+
+kda_status validate_prefill(const kda_prefill_desc *d, PrefillPlan *p) {
+  kda_status st0 = validate_sizes(d);
+  if (st0 != KDA_OK) return st0;
+  const size_t ntok = static_cast<size_t>(d->B) * d->T * d->H;
+  const size_t nstate = static_cast<size_t>(d->B) * d->H;
+  const int64_t n_ckpt = d->ckpt_every > 0 ? d->T / d->ckpt_every : 0;
+  if (ntok > 0 && (!d->q || !d->k || !d->v || !d->g || !d->beta || !d->o)) return KDA_ERR_NULL;
+  if (n_ckpt > 0 && nstate > 0 && !d->ckpt) return KDA_ERR_NULL;
+  kda_status st = plan_prefill(*d, p);
+  if (st != KDA_OK) return st;
+
+  // aliasing
+  const size_t ie = esize(d->in_dtype), oe = esize(d->out_dtype);
+  const size_t dk = d->d_k, dv = d->d_v, sbytes = nstate * dk * dv * 4;
+  const size_t o_bytes = ntok * dv * oe;
+  const size_t ck_bytes = static_cast<size_t>(n_ckpt) * sbytes;
+  struct R { const void *p; size_t n; } in[] = {
+      {d->q, ntok * dk * ie}, {d->k, ntok * dk * ie}, {d->v, ntok * dv * ie},
+      {d->g, ntok * dk * 4},  {d->beta, ntok * 4},    {d->gate, d->gate ? ntok * dv * ie : 0},
+      {d->S0, d->S0 ? sbytes : 0}, {d->norm_weight, d->norm_weight ? dv * 4 : 0}};
+  for (const R &r : in)
+    if (overlap(d->o, o_bytes, r.p, r.n)) return KDA_ERR_ALIAS;
+  if (overlap(d->o, o_bytes, d->S_final, d->S_final ? sbytes : 0)) return KDA_ERR_ALIAS;
+  if (overlap(d->o, o_bytes, d->ckpt, ck_bytes)) return KDA_ERR_ALIAS;
+  if (d->S_final) {
+    for (int i = 0; i < 6; ++i)
+      if (overlap(d->S_final, sbytes, in[i].p, in[i].n)) return KDA_ERR_ALIAS;
+    if (d->S0 && d->S_final != d->S0 && overlap(d->S_final, sbytes, d->S0, sbytes)) return KDA_ERR_ALIAS;
+    if (overlap(d->S_final, sbytes, d->ckpt, ck_bytes)) return KDA_ERR_ALIAS;
+  }
+  if (d->ckpt) {
+    for (const R &r : in)
+      if (overlap(d->ckpt, ck_bytes, r.p, r.n)) return KDA_ERR_ALIAS;
+  }
+  if (p->ws_total > 0) {
+    if (!d->workspace || d->workspace_bytes < p->ws_total) return KDA_ERR_WORKSPACE;
+    for (const R &r : in)
+      if (overlap(d->workspace, p->ws_total, r.p, r.n)) return KDA_ERR_ALIAS;
+    if (overlap(d->workspace, p->ws_total, d->o, o_bytes) ||
+        overlap(d->workspace, p->ws_total, d->S_final, d->S_final ? sbytes : 0) ||
+        overlap(d->workspace, p->ws_total, d->ckpt, ck_bytes))
+      return KDA_ERR_ALIAS;
+  }
+  return KDA_OK;
+}
+
+kda_status validate_decode(const kda_decode_desc *d) {
+  if (!d) return KDA_ERR_NULL;
+  if (d->N < 0 || d->H < 0) return KDA_ERR_SHAPE;
+  if (d->d_k != 128 || d->d_v != 128) return KDA_ERR_UNSUPPORTED;
+  if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return KDA_ERR_UNSUPPORTED;
+  const size_t n = static_cast<size_t>(d->N) * d->H;
+  if (n == 0) return KDA_OK;
+  if (!d->q || !d->k || !d->v || !d->g || !d->beta || !d->state || !d->o) return KDA_ERR_NULL;
+  const size_t ie = esize(d->in_dtype), oe = esize(d->out_dtype);
+  const size_t dk = d->d_k, dv = d->d_v;
+  const size_t o_bytes = n * dv * oe, s_bytes = n * dk * dv * 4;
+  struct R { const void *p; size_t n; } in[] = {
+      {d->q, n * dk * ie}, {d->k, n * dk * ie}, {d->v, n * dv * ie}, {d->g, n * dk * 4},
+      {d->beta, n * 4},    {d->gate, d->gate ? n * dv * ie : 0},
+      {d->norm_weight, d->norm_weight ? dv * 4 : 0}, {d->state, s_bytes}};
+  for (const R &r : in)
+    if (overlap(d->o, o_bytes, r.p, r.n)) return KDA_ERR_ALIAS;
+  for (int i = 0; i < 7; ++i)
+    if (overlap(d->state, s_bytes, in[i].p, in[i].n)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+kda_status validate_copy(const float *a, const float *b, int64_t n_states, int32_t dk, int32_t dv) {
+  if (n_states < 0 || dk < 1 || dv < 1) return KDA_ERR_SHAPE;
+  if (n_states == 0) return KDA_OK;
+  if (!a || !b) return KDA_ERR_NULL;
+  const size_t bytes = static_cast<size_t>(n_states) * dk * dv * 4;
+  if (overlap(a, bytes, b, bytes)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_prefill_workspace_size(const kda_prefill_desc *d, size_t *bytes) {
+  if (!bytes) return KDA_ERR_NULL;
+  kda_status st = validate_sizes(d);
+  if (st != KDA_OK) return st;
+  PrefillPlan p;
+  st = plan_prefill(*d, &p);
+  if (st != KDA_OK) return st;
+  *bytes = p.ws_total;
+  return KDA_OK;
+}
+
+kda_status kda_prefill_chunked(const kda_prefill_desc *d, hipStream_t stream) {
+  PrefillPlan p;
+  kda_status st = validate_prefill(d, &p);
+  if (st != KDA_OK) return st;
+  if (static_cast<int64_t>(d->B) * d->H == 0) return KDA_OK;
+  st = check_device();
+  if (st != KDA_OK) return st;
+  return from_hip(kda::launch_prefill(*d, p, stream));
+}
+
+kda_status kda_decode_step(const kda_decode_desc *d, hipStream_t stream) {
+  kda_status st = validate_decode(d);
+  if (st != KDA_OK) return st;
+  if (static_cast<int64_t>(d->N) * d->H == 0) return KDA_OK;
+  st = check_device();
+  if (st != KDA_OK) return st;
+  return from_hip(kda::launch_decode(*d, stream));
+}
+
+kda_status kda_state_checkpoint(const float *state, float *ckpt, int64_t n_states, int32_t d_k,
+                                int32_t d_v, hipStream_t stream) {
+  kda_status st = validate_copy(state, ckpt, n_states, d_k, d_v);
+  if (st != KDA_OK || n_states == 0) return st;
+  st = check_device();
+  if (st != KDA_OK) return st;
+  return from_hip(kda::launch_state_copy(ckpt, state, n_states * d_k * d_v, stream));
+}
+
+kda_status kda_state_rollback(float *state, const float *ckpt, int64_t n_states, int32_t d_k,
+                              int32_t d_v, hipStream_t stream) {
+  kda_status st = validate_copy(state, ckpt, n_states, d_k, d_v);
+  if (st != KDA_OK || n_states == 0) return st;
+  st = check_device();
+  if (st != KDA_OK) return st;
+  return from_hip(kda::launch_state_copy(state, ckpt, n_states * d_k * d_v, stream));
+}
+
+const char *kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "a required pointer is NULL";
+    case KDA_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration (d_k/d_v must be 128; chunk 16 or 64; dtype f32 or bf16)";
+    case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+    case KDA_ERR_ALIAS: return "an output buffer overlaps a buffer it must not overlap";
+    case KDA_ERR_DEVICE: return "current HIP device is not gfx950 (MI355X) or cannot be queried";
+    case KDA_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+// KDA recurrent decode step (the recurrent form; "xhh.club" tag page 结构, entries on
+// the recurrent form and on the chunkwise algorithm: decode uses the recurrent form).
+//
+// One workgroup owns one (sequence, head) state of 128 x 128 fp32 (64 KB).  The state
+// is the only large operand, so the step is bound by HBM: it is read once and written
+// once, in place, with 16-byte loads and stores that cover whole 512-byte rows per half
+// wave.  Both reductions over the key axis come from one read of the state, using
+//     o = S_new^T q = S'^T q + u (k . q),   with  S' = Diag(alpha) S,
+// so e = S'^T k and f = S'^T q are reduced together, then u = beta (v - e) and the
+// write S_new = S' + k u^T reuse the values still held in registers.
+//
+// Thread layout (256 threads): column group cg = tid % 32 owns columns 4cg..4cg+3;
+// row phase rp = tid / 32 owns rows rp, rp+8, ..., rp+120 (16 rows).
+#include "internal.h"
+#include "kda_device.h"
+
+namespace kda {
+namespace {
+
+constexpr int D = 128;
+constexpr int NT = 256;
+constexpr int ROWS_PER_T = D / 8;   // 16 rows per thread
+
+struct DecodeArgs {
+  const void *q, *k, *v, *gate;
+  const float *g, *beta, *norm_weight;
+  float *state;
+  void *o;
+  float eps;
+};
+
+template <bool IN_BF16, bool OUT_BF16, bool GATE>
+__global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
+  __shared__ float s_alpha[D], s_k[D], s_q[D];
+  __shared__ float s_red[4][32][9];
+  __shared__ float s_sq[4];
+
+  const int tid = threadIdx.x;
+  const int cg = tid & 31, rp = tid >> 5, wave = tid >> 6, lane = tid & 63;
+  const size_t nh = blockIdx.x;                       // sequence * H + head
+  float *S = a.state + nh * (size_t)(D * D);
+
+  // Issue the 16 state loads first so their latency overlaps the small vector loads.
+  float4 s[ROWS_PER_T];
+#pragma unroll
+  for (int m = 0; m < ROWS_PER_T; ++m)
+    s[m] = *reinterpret_cast<const float4 *>(S + (size_t)(rp + 8 * m) * D + 4 * cg);
+
+  if (tid < D) {
+    const size_t i = nh * D + tid;
+    s_alpha[tid] = exp2_fast(log2_decay(a.g[i]));
+    s_k[tid] = load1<IN_BF16>(a.k, i);
+    s_q[tid] = load1<IN_BF16>(a.q, i);
+  }
+  const float4 vv = load4<IN_BF16>(a.v, nh * D + 4 * cg);
+  const float bt = a.beta[nh];
+  __syncthreads();
+
+  // Decay the rows, then partial reductions e = S'^T k, f = S'^T q and k.q.
+  float4 e = make_float4(0.f, 0.f, 0.f, 0.f), f = e;
+  float kq = 0.f;
+#pragma unroll
+  for (int m = 0; m < ROWS_PER_T; ++m) {
+    const int i = rp + 8 * m;
+    const float al = s_alpha[i], kk = s_k[i], qq = s_q[i];
+    s[m].x *= al; s[m].y *= al; s[m].z *= al; s[m].w *= al;
+    e.x += s[m].x * kk; e.y += s[m].y * kk; e.z += s[m].z * kk; e.w += s[m].w * kk;
+    f.x += s[m].x * qq; f.y += s[m].y * qq; f.z += s[m].z * qq; f.w += s[m].w * qq;
+    kq += kk * qq;
+  }
+  // Sum the two row phases of this wave (lanes l and l ^ 32), then the four waves.
+  float r[9] = {e.x, e.y, e.z, e.w, f.x, f.y, f.z, f.w, kq};
+#pragma unroll
+  for (int j = 0; j < 9; ++j) r[j] += __shfl_xor(r[j], 32, 64);
+  if (lane < 32) {
+#pragma unroll
+    for (int j = 0; j < 9; ++j) s_red[wave][cg][j] = r[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 9; ++j) r[j] = s_red[0][cg][j] + s_red[1][cg][j] + s_red[2][cg][j] + s_red[3][cg][j];
+
+  const float4 u = make_float4(bt * (vv.x - r[0]), bt * (vv.y - r[1]), bt * (vv.z - r[2]),
+                               bt * (vv.w - r[3]));
+  kq = r[8];
+  // Write S_new = S' + k u^T.
+#pragma unroll
+  for (int m = 0; m < ROWS_PER_T; ++m) {
+    const int i = rp + 8 * m;
+    const float kk = s_k[i];
+    float4 x = s[m];
+    x.x += kk * u.x; x.y += kk * u.y; x.z += kk * u.z; x.w += kk * u.w;
+    *reinterpret_cast<float4 *>(S + (size_t)i * D + 4 * cg) = x;
+  }
+
+  float4 o = make_float4(r[4] + u.x * kq, r[5] + u.y * kq, r[6] + u.z * kq, r[7] + u.w * kq);
+  if constexpr (GATE) {
+    // Per-head RMSNorm over the 128 value columns, then the sigmoid gate.
+    float sq = o.x * o.x + o.y * o.y + o.z * o.z + o.w * o.w;
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) sq += __shfl_xor(sq, off, 64);
+    if (tid == 0) s_sq[0] = sq;
+    __syncthreads();
+    const float inv = rsqrtf(s_sq[0] * (1.0f / D) + a.eps);
+    const float4 gt = load4<IN_BF16>(a.gate, nh * D + 4 * cg);
+    float4 w = make_float4(1.f, 1.f, 1.f, 1.f);
+    if (a.norm_weight) w = *reinterpret_cast<const float4 *>(a.norm_weight + 4 * cg);
+    o.x *= inv * w.x * sigmoidf_(gt.x);
+    o.y *= inv * w.y * sigmoidf_(gt.y);
+    o.z *= inv * w.z * sigmoidf_(gt.z);
+    o.w *= inv * w.w * sigmoidf_(gt.w);
+  }
+  if (rp == 0) store4<OUT_BF16>(a.o, nh * D + 4 * cg, o);
+}
+
+template <bool IN_BF16, bool OUT_BF16, bool GATE>
+hipError_t launch3(const DecodeArgs &a, unsigned n_blocks, hipStream_t s) {
+  hipLaunchKernelGGL((decode_kernel<IN_BF16, OUT_BF16, GATE>), dim3(n_blocks), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const kda_decode_desc &d, hipStream_t s) {
+  const int64_t n = (int64_t)d.N * d.H;
+  if (n == 0) return hipSuccess;
+  DecodeArgs a{d.q, d.k, d.v, d.gate, d.g, d.beta, d.norm_weight, d.state, d.o, d.norm_eps};
+  const bool ib = d.in_dtype == KDA_BF16, ob = d.out_dtype == KDA_BF16, gt = d.gate != nullptr;
+  const unsigned nb = static_cast<unsigned>(n);
+  if (ib) {
+    if (ob) return gt ? launch3<true, true, true>(a, nb, s) : launch3<true, true, false>(a, nb, s);
+    return gt ? launch3<true, false, true>(a, nb, s) : launch3<true, false, false>(a, nb, s);
+  }
+  if (ob) return gt ? launch3<false, true, true>(a, nb, s) : launch3<false, true, false>(a, nb, s);
+  return gt ? launch3<false, false, true>(a, nb, s) : launch3<false, false, false>(a, nb, s);
+}
+
+}  // namespace kda

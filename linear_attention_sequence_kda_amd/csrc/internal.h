@@ -1,0 +1,30 @@
+// Launchers shared between the host ABI layer (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+hipError_t launch_decode(const kda_decode_desc &d, hipStream_t s);
+hipError_t launch_state_copy(float *dst, const float *src, int64_t n_floats, hipStream_t s);
+
+// Execution plan of one prefill call, decided on the host.
+struct PrefillPlan {
+  int n_seg;        // segments per sequence (1 = no context parallelism)
+  int seg_chunks;   // chunks per segment (last segment may be shorter)
+  int n_chunks;     // chunks per sequence
+  int v_split;      // workgroups per (sequence, head, segment) over the value columns
+  bool split_norm;  // norm/gate epilogue runs as a separate pass (v_split > 1 with a gate)
+  size_t ws_maps;   // bytes: segment maps [B,H,n_seg,d_k,2*d_v] fp32
+  size_t ws_sin;    // bytes: states entering each segment [B,H,n_seg,d_k,d_v] fp32
+  size_t ws_norm;   // bytes: per-token partial sums of squares [B,T,H,v_split] fp32
+  size_t ws_total;
+};
+
+hipError_t launch_prefill(const kda_prefill_desc &d, const PrefillPlan &p, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,144 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol that
+include/kda.h declares, and rejects bad arguments synchronously before touching a
+device.  Fake pointers used here are never dereferenced: every call either fails
+validation or (with no GPU) fails the device check."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import linear_attention_sequence_kda_amd as kda
+from linear_attention_sequence_kda_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    return sorted(set(re.findall(r"KDA_API\s+[\w\s\*]+?\b(kda_\w+)\s*\(", src)))
+
+
+def test_header_declares_entry_points():
+    names = _declared()
+    for n in ("kda_prefill_chunked", "kda_decode_step", "kda_state_checkpoint",
+              "kda_state_rollback", "kda_prefill_workspace_size", "kda_status_string",
+              "kda_abi_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = C.CDLL(_lib.LIB_PATH)
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    assert kda.kda_abi_version() == 1
+    seen = set()
+    for st in range(8):
+        s = kda.status_string(st)
+        assert s and s not in seen
+        seen.add(s)
+    assert kda.status_string(99) == "unknown status"
+
+
+FAKE = 1 << 40   # never dereferenced
+
+
+def _desc(**over):
+    d = _lib.PrefillDesc()
+    d.B, d.T, d.H, d.d_k, d.d_v, d.chunk = 2, 128, 4, 128, 128, 64
+    d.in_dtype, d.out_dtype = _lib.KDA_BF16, _lib.KDA_F32
+    n = 2 * 128 * 4 * 128
+    base = FAKE
+    d.q, d.k, d.v = base, base + 2 * n, base + 4 * n
+    d.g, d.beta = base + 6 * n, base + 10 * n
+    d.o = base + 20 * n
+    d.v_split, d.n_segments = 1, 1
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def _call(d):
+    return _lib.load().kda_prefill_chunked(C.byref(d), None)
+
+
+def _gpu_present():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+def test_prefill_validation_errors():
+    lib = _lib.load()
+    assert lib.kda_prefill_chunked(None, None) == kda.KDA_ERR_NULL
+    assert _call(_desc(d_k=64)) == kda.KDA_ERR_UNSUPPORTED
+    assert _call(_desc(chunk=32)) == kda.KDA_ERR_UNSUPPORTED
+    assert _call(_desc(in_dtype=7)) == kda.KDA_ERR_UNSUPPORTED
+    assert _call(_desc(v_split=3)) == kda.KDA_ERR_UNSUPPORTED
+    assert _call(_desc(B=-1)) == kda.KDA_ERR_SHAPE
+    assert _call(_desc(ckpt_every=100)) == kda.KDA_ERR_SHAPE
+    assert _call(_desc(n_segments=3)) == kda.KDA_ERR_SHAPE           # 2 chunks only
+    assert _call(_desc(q=None)) == kda.KDA_ERR_NULL
+    assert _call(_desc(ckpt_every=64)) == kda.KDA_ERR_NULL            # ckpt missing
+    d = _desc()
+    d.o = d.k + 100                                                  # o overlaps k
+    assert _call(d) == kda.KDA_ERR_ALIAS
+    d = _desc(n_segments=2)                                          # needs a workspace
+    assert _call(d) == kda.KDA_ERR_WORKSPACE
+    n = C.c_size_t(0)
+    assert lib.kda_prefill_workspace_size(C.byref(d), C.byref(n)) == kda.KDA_OK
+    assert n.value >= 2 * 4 * 2 * 3 * 128 * 128 * 4
+    d.workspace, d.workspace_bytes = FAKE + (1 << 36), n.value - 1
+    assert _call(d) == kda.KDA_ERR_WORKSPACE
+    assert lib.kda_prefill_workspace_size(C.byref(_desc()), None) == kda.KDA_ERR_NULL
+
+
+def test_empty_prefill_is_a_noop():
+    # B*H == 0 returns before the device check
+    assert _call(_desc(B=0)) == kda.KDA_OK
+
+
+@pytest.mark.skipif(_gpu_present(), reason="checks the no-device error path")
+def test_prefill_without_device_reports_device_error():
+    assert _call(_desc()) == kda.KDA_ERR_DEVICE
+
+
+def _ddesc(**over):
+    d = _lib.DecodeDesc()
+    d.N, d.H, d.d_k, d.d_v = 4, 2, 128, 128
+    d.in_dtype, d.out_dtype = _lib.KDA_BF16, _lib.KDA_F32
+    n = 4 * 2 * 128
+    d.q, d.k, d.v, d.g, d.beta = FAKE, FAKE + 2 * n, FAKE + 4 * n, FAKE + 6 * n, FAKE + 10 * n
+    d.state, d.o = FAKE + (1 << 30), FAKE + (1 << 31)
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_decode_validation_errors():
+    lib = _lib.load()
+    f = lambda d: lib.kda_decode_step(C.byref(d), None)  # noqa: E731
+    assert lib.kda_decode_step(None, None) == kda.KDA_ERR_NULL
+    assert f(_ddesc(d_v=64)) == kda.KDA_ERR_UNSUPPORTED
+    assert f(_ddesc(N=-2)) == kda.KDA_ERR_SHAPE
+    assert f(_ddesc(state=None)) == kda.KDA_ERR_NULL
+    d = _ddesc()
+    d.o = d.q
+    assert f(d) == kda.KDA_ERR_ALIAS
+    d = _ddesc()
+    d.state = d.v
+    assert f(d) == kda.KDA_ERR_ALIAS
+    assert f(_ddesc(N=0)) == kda.KDA_OK
+
+
+def test_copy_validation_errors():
+    lib = _lib.load()
+    assert lib.kda_state_checkpoint(FAKE, FAKE + 8, 1, 128, 128, None) == kda.KDA_ERR_ALIAS
+    assert lib.kda_state_rollback(None, FAKE, 1, 128, 128, None) == kda.KDA_ERR_NULL
+    assert lib.kda_state_rollback(FAKE, FAKE + (1 << 20), -1, 128, 128, None) == kda.KDA_ERR_SHAPE
+    assert lib.kda_state_checkpoint(FAKE, FAKE + (1 << 20), 0, 128, 128, None) == kda.KDA_OK
