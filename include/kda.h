@@ -95,7 +95,7 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
 typedef struct kda_prefill_desc {
   int32_t B, T, H;          /* T >= 0; any T (a ragged last chunk is handled) */
   int32_t d_k, d_v;         /* must be 128 */
-  int32_t chunk;            /* 16 or 64 tokens per chunk */
+  int32_t chunk;            /* 16 or 64 tokens per chunk (16 when in_dtype = KDA_F32) */
   int32_t in_dtype;         /* kda_dtype of q, k, v and gate */
   int32_t out_dtype;        /* kda_dtype of o */
   const void *q;            /* [B,T,H,d_k] */
@@ -116,7 +116,8 @@ typedef struct kda_prefill_desc {
                                that many segments combined by an associative scan of
                                their state maps ([S], [G]) */
   int32_t v_split;          /* 0 = choose; else 1, 2 or 4 workgroups per (seq, head)
-                               splitting the d_v columns of the state */
+                               splitting the d_v columns of the state (fp32 inputs use
+                               at least 2) */
   void *workspace;          /* device scratch of kda_prefill_workspace_size() bytes */
   size_t workspace_bytes;
 } kda_prefill_desc;

@@ -61,6 +61,7 @@ kda_status plan_prefill(const kda_prefill_desc &d, PrefillPlan *p) {
     vs = 1;
     while (vs < 4 && units * vs * 2 <= kTargetWorkgroups) vs *= 2;
   }
+  if (d.in_dtype == KDA_F32 && vs < 2) vs = 2;   // fp32 operands: at most 64 columns per workgroup
   p->v_split = vs;
 
   // segments
@@ -84,8 +85,8 @@ kda_status plan_prefill(const kda_prefill_desc &d, PrefillPlan *p) {
     p->ws_maps = static_cast<size_t>(units) * p->n_seg * dkdv * 2 * sizeof(float);
     p->ws_sin = static_cast<size_t>(units) * p->n_seg * dkdv * sizeof(float);
   }
-  if (p->split_norm)
-    p->ws_norm = static_cast<size_t>(units) * static_cast<size_t>(d.T) * vs * sizeof(float);
+  if (p->split_norm && d.out_dtype == KDA_BF16)
+    p->ws_norm = static_cast<size_t>(units) * static_cast<size_t>(d.T) * d.d_v * sizeof(float);
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   p->ws_total = up(p->ws_maps) + up(p->ws_sin) + up(p->ws_norm);
   return KDA_OK;
@@ -97,6 +98,7 @@ kda_status validate_sizes(const kda_prefill_desc *d) {
   if (d->d_k != 128 || d->d_v != 128) return KDA_ERR_UNSUPPORTED;
   if (d->chunk != 16 && d->chunk != 64) return KDA_ERR_UNSUPPORTED;
   if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return KDA_ERR_UNSUPPORTED;
+  if (d->in_dtype == KDA_F32 && d->chunk != 16) return KDA_ERR_UNSUPPORTED;
   if (d->v_split != 0 && d->v_split != 1 && d->v_split != 2 && d->v_split != 4)
     return KDA_ERR_UNSUPPORTED;
   if (d->n_segments < 0) return KDA_ERR_SHAPE;
@@ -129,8 +131,8 @@ kda_status validate_prefill(const kda_prefill_desc *d, PrefillPlan *p) {
   if (overlap(d->o, o_bytes, d->S_final, d->S_final ? sbytes : 0)) return KDA_ERR_ALIAS;
   if (overlap(d->o, o_bytes, d->ckpt, ck_bytes)) return KDA_ERR_ALIAS;
   if (d->S_final) {
-    for (int i = 0; i < 6; ++i)
-      if (overlap(d->S_final, sbytes, in[i].p, in[i].n)) return KDA_ERR_ALIAS;
+    for (int i = 0; i < 8; ++i)
+      if (i != 6 && overlap(d->S_final, sbytes, in[i].p, in[i].n)) return KDA_ERR_ALIAS;
     if (d->S0 && d->S_final != d->S0 && overlap(d->S_final, sbytes, d->S0, sbytes)) return KDA_ERR_ALIAS;
     if (overlap(d->S_final, sbytes, d->ckpt, ck_bytes)) return KDA_ERR_ALIAS;
   }

@@ -11,6 +11,7 @@ namespace kda {
 
 hipError_t launch_decode(const kda_decode_desc &d, hipStream_t s);
 hipError_t launch_state_copy(float *dst, const float *src, int64_t n_floats, hipStream_t s);
+hipError_t launch_fill_zero(float *dst, int64_t n_floats, hipStream_t s);
 
 // Execution plan of one prefill call, decided on the host.
 struct PrefillPlan {
@@ -21,7 +22,7 @@ struct PrefillPlan {
   bool split_norm;  // norm/gate epilogue runs as a separate pass (v_split > 1 with a gate)
   size_t ws_maps;   // bytes: segment maps [B,H,n_seg,d_k,2*d_v] fp32
   size_t ws_sin;    // bytes: states entering each segment [B,H,n_seg,d_k,d_v] fp32
-  size_t ws_norm;   // bytes: per-token partial sums of squares [B,T,H,v_split] fp32
+  size_t ws_norm;   // bytes: raw fp32 outputs [B,T,H,d_v] for the separate norm pass (bf16 out)
   size_t ws_total;
 };
 

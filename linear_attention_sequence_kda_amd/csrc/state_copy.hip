@@ -21,6 +21,11 @@ __global__ __launch_bounds__(256) void copy_scalar(float *__restrict__ dst,
     dst[i] = src[i];
 }
 
+__global__ __launch_bounds__(256) void fill_zero(float *__restrict__ dst, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) dst[i] = 0.f;
+}
+
 unsigned grid_for(int64_t n) {
   const int64_t blocks = (n + 255) / 256;
   return static_cast<unsigned>(blocks < 4096 ? (blocks < 1 ? 1 : blocks) : 4096);
@@ -38,6 +43,12 @@ hipError_t launch_state_copy(float *dst, const float *src, int64_t n, hipStream_
   } else {
     hipLaunchKernelGGL(copy_scalar, dim3(grid_for(n)), dim3(256), 0, s, dst, src, n);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(float *dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_zero, dim3(grid_for(n)), dim3(256), 0, s, dst, n);
   return hipGetLastError();
 }
 

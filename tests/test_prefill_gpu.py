@@ -1,0 +1,222 @@
+"""GPU parity of the chunkwise prefill, through the C ABI, against the fp64 CPU oracle
+on the same seeded input bytes.
+
+Tolerances (floating point, no single correct rounding):
+  bf16 inputs (BF16/fp16 MFMA):  err_o <= 2e-2, err_S <= 1e-2
+  fp32 inputs (fp32 MFMA):       err_o <= 1e-4, err_S <= 1e-4
+err_o = max|o - o_ref| / rms(o_ref), err_S = ||S - S_ref||_F / ||S_ref||_F.  Outputs
+are stored in fp32 unless a test says otherwise (bf16 storage adds up to 2^-8 of the
+largest |o|).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_sequence_kda_amd as kda
+from kda_inputs import BF16, F32, make_prefill, to_f64
+from oracle import native, norm_gate
+from gpu_util import up, down, err_o, err_S, bf16_out_tol, dev
+
+pytestmark = pytest.mark.gpu
+
+TOL_O_BF16, TOL_S_BF16 = 2e-2, 1e-2
+TOL_O_F32, TOL_S_F32 = 1e-4, 1e-4
+
+
+def _say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+def run_gpu(c, *, chunk=64, out_dtype=torch.float32, v_split=0, n_segments=0, ckpt_every=0,
+            gate=False, norm_weight=None, eps=1e-6, S0=True):
+    B, T, H = c.B, c.T, c.H
+    o = torch.full((B, T, H, 128), float("nan"), dtype=out_dtype, device=dev())
+    Sf = torch.full((B, H, 128, 128), float("nan"), dtype=torch.float32, device=dev())
+    ck = None
+    if ckpt_every:
+        ck = torch.full((B, T // ckpt_every, H, 128, 128), float("nan"), device=dev())
+    kda.kda_prefill_chunked(up(c.q), up(c.k), up(c.v), up(c.g), up(c.beta), o=o,
+                            S0=up(c.S0) if S0 else None, S_final=Sf,
+                            gate=up(c.gate) if gate else None,
+                            norm_weight=None if norm_weight is None else up(norm_weight),
+                            norm_eps=eps, chunk=chunk, ckpt_every=ckpt_every, ckpt=ck,
+                            n_segments=n_segments, v_split=v_split)
+    torch.cuda.synchronize()
+    return o, Sf, ck
+
+
+def run_ref(c, *, ckpt_every=0, gate=False, norm_weight=None, eps=1e-6, S0=True):
+    o, S, ck = native.prefill(c.q, c.k, c.v, c.g, c.beta, c.S0 if S0 else None,
+                              bf16=(c.in_dtype == BF16), ckpt_every=ckpt_every)
+    if gate:
+        o = norm_gate(o, to_f64(c.gate, c.in_dtype), eps, norm_weight)
+    return o, S, ck
+
+
+def check(c, label, tol_o=TOL_O_BF16, tol_s=TOL_S_BF16, **kw):
+    gate = kw.get("gate", False)
+    o, S, ck = run_gpu(c, **kw)
+    o_ref, S_ref, ck_ref = run_ref(c, ckpt_every=kw.get("ckpt_every", 0), gate=gate,
+                                   norm_weight=kw.get("norm_weight"), S0=kw.get("S0", True))
+    og = down(o)
+    eo, es = err_o(og, o_ref), err_S(down(S), S_ref)
+    tol = tol_o if kw.get("out_dtype", torch.float32) == torch.float32 else bf16_out_tol(o_ref, tol_o)
+    _say(f"{label}: err_o={eo:.3e} err_S={es:.3e}")
+    assert np.isfinite(og).all(), "non-finite output"
+    assert eo <= tol, (label, eo)
+    assert es <= tol_s, (label, es)
+    if ck is not None:
+        for m in range(ck_ref.shape[1]):
+            e = err_S(down(ck[:, m]), ck_ref[:, m])
+            assert e <= tol_s, (label, "ckpt", m, e)
+    return o, S
+
+
+# ---------------------------------------------------------------------------
+# small cases spanning several tiles and ragged tails
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 64, 100, 200])
+@pytest.mark.parametrize("chunk", [16, 64])
+def test_bf16_small_ragged(T, chunk):
+    c = make_prefill(2, T, 2, 128, seed=T + chunk, in_dtype=BF16, s0_std=0.05)
+    check(c, f"bf16 T={T} chunk={chunk}", chunk=chunk, v_split=1)
+
+
+@pytest.mark.parametrize("v_split", [1, 2, 4])
+def test_bf16_v_split(v_split):
+    c = make_prefill(1, 300, 3, 128, seed=11, in_dtype=BF16, s0_std=0.05)
+    check(c, f"bf16 v_split={v_split}", chunk=64, v_split=v_split)
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_f32_tiny_workload(seed):
+    """Tiny fp32 workload: B=1, H=2, T=256, chunk 16, S0 = 0."""
+    c = make_prefill(1, 256, 2, 128, seed=seed, in_dtype=F32)
+    check(c, f"f32 tiny seed={seed}", TOL_O_F32, TOL_S_F32, chunk=16, S0=False)
+
+
+def test_f32_ragged_with_state():
+    c = make_prefill(2, 37, 3, 128, seed=5, in_dtype=F32, s0_std=0.1)
+    check(c, "f32 ragged", TOL_O_F32, TOL_S_F32, chunk=16, v_split=4)
+
+
+def test_bf16_on_tiny_shapes():
+    c = make_prefill(1, 256, 2, 128, seed=0, in_dtype=BF16)
+    check(c, "bf16 tiny chunk16", chunk=16, S0=False)
+    check(c, "bf16 tiny chunk64", chunk=64, S0=False)
+
+
+# ---------------------------------------------------------------------------
+# decay floor and special cases
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["floor", "zero", "below_floor", "raw"])
+def test_decay_modes(mode):
+    c = make_prefill(1, 192, 2, 128, seed=21, in_dtype=BF16, s0_std=0.1, g_mode=mode)
+    check(c, f"g={mode}", chunk=64)
+
+
+def test_below_floor_equals_floor():
+    a = make_prefill(1, 128, 2, 128, seed=22, in_dtype=BF16, s0_std=0.1, g_mode="floor")
+    b = make_prefill(1, 128, 2, 128, seed=22, in_dtype=BF16, s0_std=0.1, g_mode="below_floor")
+    oa, Sa, _ = run_gpu(a)
+    ob, Sb, _ = run_gpu(b)
+    assert torch.equal(oa, ob) and torch.equal(Sa, Sb)
+
+
+def test_beta_zero_only_decays():
+    c = make_prefill(2, 150, 2, 128, seed=23, in_dtype=BF16, s0_std=0.1, beta_mode="zero")
+    check(c, "beta=0", chunk=64)
+
+
+def test_beta_one():
+    c = make_prefill(1, 150, 2, 128, seed=24, in_dtype=BF16, s0_std=0.1, beta_mode="one")
+    check(c, "beta=1", chunk=64)
+
+
+# ---------------------------------------------------------------------------
+# norm + gate, checkpoints, segments
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("v_split", [1, 4])
+def test_norm_gate(v_split):
+    c = make_prefill(2, 320, 2, 128, seed=31, in_dtype=BF16, s0_std=0.01, gate=True)
+    w = np.random.default_rng(31).uniform(0.5, 1.5, 128).astype(np.float32)
+    check(c, f"gate v_split={v_split}", chunk=64, v_split=v_split, gate=True, norm_weight=w)
+    check(c, f"gate v_split={v_split} bf16 out", chunk=64, v_split=v_split, gate=True,
+          out_dtype=torch.bfloat16)
+
+
+def test_checkpoints():
+    c = make_prefill(2, 640, 2, 128, seed=41, in_dtype=BF16, s0_std=0.05)
+    check(c, "ckpt every 128", chunk=64, ckpt_every=128)
+
+
+@pytest.mark.parametrize("n_seg", [2, 3, 8])
+def test_segments(n_seg):
+    c = make_prefill(1, 1024, 2, 128, seed=51, in_dtype=BF16, s0_std=0.05)
+    check(c, f"segments={n_seg}", chunk=64, n_segments=n_seg, ckpt_every=256)
+
+
+def test_segments_slow_decay():
+    c = make_prefill(1, 2048, 2, 128, seed=52, in_dtype=BF16, pinned_floor_frac=0.1,
+                     slow_frac=0.1)
+    check(c, "segments slow decay", chunk=64, n_segments=8, S0=False)
+
+
+def test_segment_count_agreement():
+    c = make_prefill(1, 1024, 2, 128, seed=53, in_dtype=BF16, s0_std=0.05)
+    outs = [run_gpu(c, n_segments=n) for n in (1, 2, 4, 16)]
+    for o, S, _ in outs[1:]:
+        assert err_o(down(o), down(outs[0][0])) <= 1e-2
+        assert err_S(down(S), down(outs[0][1])) <= 1e-2
+
+
+def test_deterministic():
+    c = make_prefill(2, 200, 2, 128, seed=61, in_dtype=BF16, s0_std=0.05, gate=True)
+    o1, S1, _ = run_gpu(c, gate=True, v_split=2)
+    o2, S2, _ = run_gpu(c, gate=True, v_split=2)
+    assert torch.equal(o1, o2) and torch.equal(S1, S2)
+
+
+def test_resume_from_checkpoint():
+    """Resume = prefill the remaining tokens from a stored checkpoint."""
+    c = make_prefill(1, 1024, 2, 128, seed=71, in_dtype=BF16, s0_std=0.05)
+    o, S, ck = run_gpu(c, ckpt_every=512)
+    tail = make_prefill(1, 1024, 2, 128, seed=71, in_dtype=BF16, s0_std=0.05)
+    for name in ("q", "k", "v", "g", "beta"):
+        setattr(tail, name, np.ascontiguousarray(getattr(tail, name)[:, 512:]))
+    tail.T = 512
+    o2 = torch.empty((1, 512, 2, 128), device=dev())
+    S2 = torch.empty((1, 2, 128, 128), device=dev())
+    kda.kda_prefill_chunked(up(tail.q), up(tail.k), up(tail.v), up(tail.g), up(tail.beta), o=o2,
+                            S0=ck[:, 0].contiguous(), S_final=S2, chunk=64)
+    torch.cuda.synchronize()
+    assert err_o(down(o2), down(o[:, 512:])) <= 1e-5
+    assert err_S(down(S2), down(S)) <= 1e-5
+
+
+def test_empty_and_errors():
+    c = make_prefill(1, 0, 2, 128, seed=0, in_dtype=BF16, s0_std=0.1)
+    o = torch.empty((1, 0, 2, 128), device=dev())
+    Sf = torch.empty((1, 2, 128, 128), device=dev())
+    S0 = up(c.S0)
+    kda.kda_prefill_chunked(up(c.q), up(c.k), up(c.v), up(c.g), up(c.beta), o=o, S0=S0, S_final=Sf)
+    torch.cuda.synchronize()
+    assert torch.equal(Sf, S0)
+    c = make_prefill(1, 64, 2, 128, seed=0, in_dtype=BF16)
+    q = up(c.q)
+    with pytest.raises(kda.KdaError) as ei:
+        kda.kda_prefill_chunked(q, up(c.k), up(c.v), up(c.g), up(c.beta), o=q)
+    assert ei.value.status == kda.KDA_ERR_ALIAS
+
+
+def test_s_final_may_alias_s0():
+    c = make_prefill(1, 200, 2, 128, seed=81, in_dtype=BF16, s0_std=0.05)
+    S = up(c.S0).clone()
+    o = torch.empty((1, 200, 2, 128), device=dev())
+    kda.kda_prefill_chunked(up(c.q), up(c.k), up(c.v), up(c.g), up(c.beta), o=o, S0=S, S_final=S,
+                            n_segments=2)
+    torch.cuda.synchronize()
+    _, S_ref, _ = run_ref(c)
+    assert err_S(down(S), S_ref) <= TOL_S_BF16
