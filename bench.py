@@ -1,0 +1,251 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Headline (`value`): chunkwise prefill tokens/s on the prefill workload B=4, H=16,
+T=8192, d=128, chunk 64, bf16 q/k/v/gate, fp32 g/beta/state, S0 ~ N(0, 0.01), with the
+fused per-head RMSNorm and sigmoid gate, fp32 output.  One step = one prefill call over
+the whole batch with inputs resident in HBM.  The same run also times the decode
+workload (256 sequences x 16 heads, fp32 states, one kernel per step) and reports its
+sequence-steps/s.
+
+Prints one JSON line with a `roofline` object for the prefill kernel (algorithmic bytes
+over measured duration against 8 TB/s) and a `cpu_baseline` object (the fp64 C oracle
+on the host cores over the same prefill workload).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16/FP16 MFMA, TFLOP/s
+D = 128
+
+
+def prefill_alg_bytes(B, T, H, out_bytes=4):
+    """Bytes the prefill must move: every input read once, every output written once."""
+    per_tok_head = 3 * D * 2 + D * 4 + 4 + D * 2 + D * out_bytes   # q,k,v bf16; g; beta; gate; o
+    states = 2 * B * H * D * D * 4                                   # S0 in, S_final out
+    return B * T * H * per_tok_head + states
+
+
+def prefill_alg_flops(B, T, H, chunk=64):
+    """Chunkwise flops per token-head: 6 d^2 (state products) + C (3 d_k + 2 d_v)
+    (intra-chunk products, triangles counted once)."""
+    return B * T * H * (6 * D * D + chunk * (3 * D + 2 * D))
+
+
+def decode_alg_bytes(N, H):
+    """Per step: state read + write, q/k/v bf16, g fp32, beta, o fp32."""
+    return N * H * (2 * D * D * 4 + 3 * D * 2 + D * 4 + 4 + D * 4)
+
+
+def _src_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "linear_attention_sequence_kda_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_from_profiles(kernel_hash):
+    """HBM bytes per prefill launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", "prefill_8k_traffic.json")
+    try:
+        with open(p) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_src_hash") != kernel_hash:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(c, gate):
+    """Time the fp64 C oracle (plus the numpy norm/gate) on the host cores."""
+    from oracle import native, norm_gate
+    from kda_inputs import to_f64
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    threads = max(1, min(cores, 64))
+    t0 = time.perf_counter()
+    o, S, _ = native.prefill(c.q, c.k, c.v, c.g, c.beta, c.S0, bf16=True, nthreads=threads)
+    norm_gate(o, to_f64(c.gate, "bf16"), 1e-6) if gate else o
+    dt = time.perf_counter() - t0
+    return dict(value=c.B * c.T / dt, unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"whole prefill workload (B={c.B}, T={c.T}, H={c.H}), fp64 C recurrence "
+                       f"+ numpy norm/gate, {dt:.1f} s")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--v-split", type=int, default=0)
+    ap.add_argument("--n-segments", type=int, default=0)
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the KDA hot path here has no multi-GPU mode "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_attention_sequence_kda_amd as kda
+    from kda_inputs import make_workload, make_decode_state, make_decode_steps
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(x):
+        x = np.ascontiguousarray(x)
+        t = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16) if x.dtype == np.uint16 \
+            else torch.from_numpy(x)
+        return t.to(dev)
+
+    # ---------------- prefill workload ----------------
+    B, T, H = 4, 8192, 16
+    c = make_workload("prefill_8k", seed=0)
+    q, k, v, g, beta, gate, S0 = (up(x) for x in (c.q, c.k, c.v, c.g, c.beta, c.gate, c.S0))
+    o = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
+    Sf = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+    kw = dict(o=o, S0=S0, S_final=Sf, gate=gate, norm_eps=1e-6, chunk=64,
+              v_split=a.v_split, n_segments=a.n_segments)
+    ws_bytes = kda.kda_prefill_workspace_size(q, k, v, g, beta, **kw)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        kda.kda_prefill_chunked(q, k, v, g, beta, workspace=ws, stream=stream, **kw)
+
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(a.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    durs = sorted(e0.elapsed_time(e1) for e0, e1 in ev)      # ms, per launch
+    ms_mean = float(np.mean(durs))
+    ms_step = wall * 1e3 / a.steps
+    tokens = B * T
+    value = tokens / (ms_step * 1e-3)
+    alg_b = prefill_alg_bytes(B, T, H)
+    alg_f = prefill_alg_flops(B, T, H)
+    kernel_ms = ms_mean
+    achieved = alg_b / (kernel_ms * 1e-3) / 1e9
+    khash = _src_hash("prefill.hip")
+    traffic = _traffic_from_profiles(khash)
+
+    out = {
+        "metric": "KDA prefill tokens/s (%MFMA peak) + decode seq-steps/s (%HBM peak), d=128",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "prefill B=4 H=16 T=8192 d=128 chunk=64; bf16 q/k/v/gate, fp32 g/beta/"
+                        "state; S0~N(0,0.01); fused per-head RMSNorm + sigmoid gate; fp32 out",
+            "global_batch": B, "seq_len": T, "heads": H, "head_dim": D, "chunk": 64,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+            "kernel": "prefill_kernel (one launch per step)",
+            "alg_bytes_per_launch": alg_b,
+            "kernel_ms_mean": round(kernel_ms, 4),
+            "kernel_ms_median": round(durs[len(durs) // 2], 4),
+        },
+        "prefill_mfma": {
+            "alg_flops_per_launch": alg_f,
+            "achieved_tflops": round(alg_f / (kernel_ms * 1e-3) / 1e12, 2),
+            "peak_tflops": BF16_PEAK_TFLOPS,
+            "frac": round(alg_f / (kernel_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+        },
+    }
+
+    # ---------------- decode workload ----------------
+    if not a.no_decode:
+        N, Hd, steps = 256, 16, a.decode_steps
+        S_np = make_decode_state(N, Hd, D, seed=0)
+        Xd = make_decode_steps(N, Hd, D, seed=0, steps=min(steps, 64))
+        X = {kk: up(vv) for kk, vv in Xd.items()}
+        St = up(S_np)
+        od = torch.empty((N, Hd, D), dtype=torch.float32, device=dev)
+        nx = X["q"].shape[0]
+
+        def dstep(s):
+            j = s % nx
+            kda.kda_decode_step(X["q"][j], X["k"][j], X["v"][j], X["g"][j], X["beta"][j], St,
+                                o=od, stream=stream)
+
+        for s in range(10):
+            dstep(s)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(steps):
+            dstep(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        db = decode_alg_bytes(N, Hd)
+        out["decode"] = {
+            "workload": "decode 256 sequences x H=16, fp32 128x128 states, bf16 q/k/v, "
+                        f"{steps} single-token steps (inputs cycle over {nx} seeded draws)",
+            "seq_steps_per_s": round(N / (us * 1e-6), 1),
+            "us_per_step": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(db / (us * 1e-6) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(db / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "alg_bytes_per_launch": db},
+        }
+
+    # one copy kernel of known size (state checkpoint, 256 MiB) after the timed regions:
+    # counter runs use it to calibrate FETCH_SIZE / WRITE_SIZE against known bytes
+    cal_src = torch.zeros((1024, D, D), dtype=torch.float32, device=dev)
+    cal_dst = torch.empty_like(cal_src)
+    kda.kda_state_checkpoint(cal_src, cal_dst, stream=stream)
+    torch.cuda.synchronize()
+
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(c, gate=True)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

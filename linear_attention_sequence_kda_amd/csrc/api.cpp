@@ -55,11 +55,15 @@ kda_status plan_prefill(const kda_prefill_desc &d, PrefillPlan *p) {
   const int64_t units = static_cast<int64_t>(d.B) * d.H;
   p->n_chunks = static_cast<int>(n_chunks);
 
-  // columns per workgroup
+  // columns per workgroup: split the value columns when (sequence, head) units alone
+  // fill at least a quarter of the chip; otherwise keep whole heads and split the
+  // sequence into segments (context parallelism), which does not repeat the
+  // per-token decay work in several workgroups
   int vs = d.v_split;
   if (vs == 0) {
-    vs = 1;
-    while (vs < 4 && units * vs * 2 <= kTargetWorkgroups) vs *= 2;
+    if (units >= kTargetWorkgroups) vs = 1;
+    else if (units * 4 >= kTargetWorkgroups) vs = units * 2 >= kTargetWorkgroups ? 2 : 4;
+    else vs = 1;
   }
   if (d.in_dtype == KDA_F32 && vs < 2) vs = 2;   // fp32 operands: at most 64 columns per workgroup
   p->v_split = vs;
@@ -69,9 +73,8 @@ kda_status plan_prefill(const kda_prefill_desc &d, PrefillPlan *p) {
   if (ns > 1 && ns > n_chunks) return KDA_ERR_SHAPE;
   if (ns == 0) {
     ns = 1;
-    // Split long sequences when (sequence, head, column slice) units cannot fill the chip
-    // and each segment still keeps >= 32 chunks.
-    while (units * vs * ns * 2 <= kTargetWorkgroups && n_chunks / (ns * 2) >= 32) ns *= 2;
+    // grow until the chip is covered, keeping >= 16 chunks per segment
+    while (units * vs * ns < kTargetWorkgroups && n_chunks / (ns * 2) >= 16) ns *= 2;
   }
   if (ns < 1) ns = 1;
   int64_t seg_chunks = n_chunks > 0 ? (n_chunks + ns - 1) / ns : 0;
