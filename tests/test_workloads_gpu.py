@@ -1,0 +1,126 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark
+times (automatic plan unless a test names one), against the fp64 CPU oracle.
+
+  prefill_8k    B=4, H=16, T=8192, chunk 64, norm + gate, S0 ~ N(0, 0.01): all heads
+  prefill_131k  B=1, H=16, T=131072, floor-pinned and slow channels, 512-token
+                checkpoints: all heads, every checkpoint
+  prefill_1m    B=1, H=8, T=2^20 over 256 segments: two sampled heads (the oracle
+                follows them token by token), then 64 decode steps on all heads with
+                a 4-step speculative rollback
+Tolerances as in test_prefill_gpu.py (bf16 inputs): err_o <= 2e-2, err_S <= 1e-2;
+decode err_o <= 1e-4.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import linear_attention_sequence_kda_amd as kda
+from kda_inputs import BF16, make_workload, make_decode_step, to_f64
+from oracle import native, norm_gate
+from gpu_util import up, down, err_o, err_S, dev
+
+pytestmark = pytest.mark.gpu
+
+TOL_O, TOL_S = 2e-2, 1e-2
+
+
+def _say(*a):
+    print(*a, flush=True, file=sys.stderr)
+
+
+@pytest.mark.parametrize("v_split", [0, 1])
+def test_prefill_8k_all_heads(v_split):
+    _say(f"prefill_8k v_split={v_split}: generating")
+    c = make_workload("prefill_8k", seed=0)
+    o = torch.empty((c.B, c.T, c.H, 128), dtype=torch.float32, device=dev())
+    S = torch.empty((c.B, c.H, 128, 128), dtype=torch.float32, device=dev())
+    kda.kda_prefill_chunked(up(c.q), up(c.k), up(c.v), up(c.g), up(c.beta), o=o, S0=up(c.S0),
+                            S_final=S, gate=up(c.gate), norm_eps=1e-6, chunk=64, v_split=v_split)
+    torch.cuda.synchronize()
+    _say("prefill_8k: oracle")
+    o_ref, S_ref, _ = native.prefill(c.q, c.k, c.v, c.g, c.beta, c.S0, bf16=True)
+    o_ref = norm_gate(o_ref, to_f64(c.gate, BF16), 1e-6)
+    og = down(o)
+    eo, es = err_o(og, o_ref), err_S(down(S), S_ref)
+    _say(f"prefill_8k v_split={v_split}: err_o={eo:.3e} err_S={es:.3e}")
+    assert np.isfinite(og).all()
+    assert eo <= TOL_O and es <= TOL_S
+
+
+def test_prefill_131k_with_checkpoints():
+    _say("prefill_131k: generating")
+    c = make_workload("prefill_131k", seed=0)
+    every = 512
+    o = torch.empty((c.B, c.T, c.H, 128), dtype=torch.float32, device=dev())
+    S = torch.empty((c.B, c.H, 128, 128), dtype=torch.float32, device=dev())
+    ck = torch.empty((c.B, c.T // every, c.H, 128, 128), dtype=torch.float32, device=dev())
+    kda.kda_prefill_chunked(up(c.q), up(c.k), up(c.v), up(c.g), up(c.beta), o=o, S_final=S,
+                            chunk=64, ckpt_every=every, ckpt=ck)
+    torch.cuda.synchronize()
+    _say("prefill_131k: oracle")
+    o_ref, S_ref, ck_ref = native.prefill(c.q, c.k, c.v, c.g, c.beta, None, bf16=True,
+                                          ckpt_every=every)
+    og = down(o)
+    eo, es = err_o(og, o_ref), err_S(down(S), S_ref)
+    ck_err = max(err_S(down(ck[:, m]), ck_ref[:, m]) for m in range(0, c.T // every, 7))
+    _say(f"prefill_131k: err_o={eo:.3e} err_S={es:.3e} max ckpt err_S={ck_err:.3e}")
+    assert np.isfinite(og).all()
+    assert eo <= TOL_O and es <= TOL_S and ck_err <= TOL_S
+    # the last checkpoint is the final state
+    assert torch.equal(ck[:, -1], S)
+
+
+def test_prefill_1m_segments_then_decode_with_rollback():
+    _say("prefill_1m: generating")
+    c = make_workload("prefill_1m", seed=0)
+    o = torch.empty((c.B, c.T, c.H, 128), dtype=torch.float32, device=dev())
+    S = torch.empty((c.B, c.H, 128, 128), dtype=torch.float32, device=dev())
+    kda.kda_prefill_chunked(up(c.q), up(c.k), up(c.v), up(c.g), up(c.beta), o=o, S_final=S,
+                            chunk=64, n_segments=256)
+    torch.cuda.synchronize()
+    heads = [1, 6]
+    _say(f"prefill_1m: oracle on heads {heads}")
+    sl = lambda x: np.ascontiguousarray(x[:, :, heads])  # noqa: E731
+    o_ref, S_ref, _ = native.prefill(sl(c.q), sl(c.k), sl(c.v), sl(c.g), sl(c.beta), None,
+                                     bf16=True)
+    og = down(o[:, :, heads])
+    eo, es = err_o(og, o_ref), err_S(down(S[:, heads]), S_ref)
+    _say(f"prefill_1m: err_o={eo:.3e} err_S={es:.3e}")
+    assert np.isfinite(og).all()
+    assert eo <= TOL_O and es <= TOL_S
+    del o, og, o_ref
+
+    # decode tail: 60 steps, checkpoint, 4 speculative steps, rollback, 4 fresh steps.
+    # GPU states continue from the GPU prefill; the oracle states from the GPU prefill
+    # final state too (the decode tolerance is for the step itself).
+    state = S[0:1].clone()                                # [N=1, H, d, d]
+    S_o = down(state)
+    od = torch.empty((1, c.H, 128), dtype=torch.float32, device=dev())
+
+    def step(s, S_o, seed):
+        st = make_decode_step(1, c.H, 128, seed=seed, step=s)
+        kda.kda_decode_step(up(st.q), up(st.k), up(st.v), up(st.g), up(st.beta), state, o=od)
+        o_r = native.decode_step(S_o, st.q, st.k, st.v, st.g, st.beta, bf16=True)
+        torch.cuda.synchronize()
+        return err_o(down(od), o_r)
+
+    worst = 0.0
+    for s in range(60):
+        worst = max(worst, step(s, S_o, 7))
+    ck = torch.empty_like(state)
+    kda.kda_state_checkpoint(state, ck)
+    S_60 = S_o.copy()
+    for s in range(60, 64):
+        step(s, S_o, 7)                                   # speculative, then rejected
+    kda.kda_state_rollback(state, ck)
+    torch.cuda.synchronize()
+    assert torch.equal(state, ck)
+    assert err_S(down(state), S_60) <= 1e-5
+    S_o = S_60
+    for s in range(60, 64):
+        worst = max(worst, step(s, S_o, 8))
+    _say(f"decode tail: worst err_o={worst:.3e}")
+    assert worst <= 1e-4
+    assert err_S(down(state), S_o) <= 1e-5
