@@ -69,7 +69,8 @@ def _traffic_from_profiles(kernel_hash):
         return None
     if t.get("kernel_src_hash") != kernel_hash:
         return None
-    return t.get("hbm_bytes_per_launch")
+    v = t.get("hbm_bytes_per_launch")
+    return None if v is None else int(v)
 
 
 def cpu_baseline(c, gate):
@@ -185,7 +186,8 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "prefill_kernel (one launch per step)",
+            "kernel": "one prefill call per step (prefill_kernel, plus norm_gate_kernel when "
+                      "the value columns of a head are split across workgroups)",
             "alg_bytes_per_launch": alg_b,
             "kernel_ms_mean": round(kernel_ms, 4),
             "kernel_ms_median": round(durs[len(durs) // 2], 4),
