@@ -237,7 +237,7 @@ def main():
                          "alg_bytes_per_launch": db},
         }
 
-    # one copy kernel of known size (state checkpoint, 256 MiB) after the timed regions:
+    # one copy kernel of known size (state checkpoint, 64 MiB each way) after the timed regions:
     # counter runs use it to calibrate FETCH_SIZE / WRITE_SIZE against known bytes
     cal_src = torch.zeros((1024, D, D), dtype=torch.float32, device=dev)
     cal_dst = torch.empty_like(cal_src)

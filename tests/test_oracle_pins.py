@@ -142,7 +142,34 @@ def pin_golden_error():
     return max(_rel(o[0, :, 0], o_ex), _rel(S[0, 0], S_ex))
 
 
+def pin_deltanet_error(seed=3, T=12, dk=6, dv=5):
+    """alpha == 1 (g = 0) is plain DeltaNet: every token takes one gradient-descent step of
+    size beta_t on the regression loss 1/2 ||S^T k_t - v_t||^2.  The gradient comes from
+    torch autograd in fp64, not from a hand-written update."""
+    import torch
+    rng = np.random.default_rng(seed)
+    q, k = rng.standard_normal((T, dk)), rng.standard_normal((T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    v = rng.standard_normal((T, dv))
+    beta = rng.uniform(0.1, 0.9, T)
+    S0 = rng.standard_normal((dk, dv))
+    S = torch.tensor(S0, dtype=torch.float64)
+    o_exp = np.zeros((T, dv))
+    for t in range(T):
+        Sv = S.clone().requires_grad_(True)
+        kt, vt = torch.tensor(k[t]), torch.tensor(v[t])
+        loss = 0.5 * torch.sum((Sv.T @ kt - vt) ** 2)
+        (grad,) = torch.autograd.grad(loss, Sv)
+        S = (S - beta[t] * grad).detach()
+        o_exp[t] = (S.T @ torch.tensor(q[t])).numpy()
+    g = np.zeros((T, dk))
+    o, Sr, _ = recurrent(q[None, :, None], k[None, :, None], v[None, :, None], g[None, :, None],
+                         beta[None, :, None], S0[None, None])
+    return max(_rel(o[0, :, 0], o_exp), _rel(Sr[0, 0], S.numpy()))
+
+
 PINS = {
+    "deltanet": (pin_deltanet_error, 1e-12),
     "exact": (pin_exact_error, 1e-12),
     "beta0": (pin_beta_zero_error, 1e-12),
     "recall": (pin_recall_error, 1e-10),
