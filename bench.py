@@ -157,7 +157,7 @@ def main():
     alg_f = prefill_alg_flops(B, T, H)
     kernel_ms = ms_mean
     achieved = alg_b / (kernel_ms * 1e-3) / 1e9
-    khash = _src_hash("prefill.hip")
+    khash = _src_hash("tiles.h", "prefill_prep.hip", "prefill_state.hip")
     traffic = _traffic_from_profiles(khash)
 
     out = {

@@ -115,10 +115,11 @@ typedef struct kda_prefill_desc {
   int32_t n_segments;       /* 0 = choose; 1 = one pass; >1 = split every sequence into
                                that many segments combined by an associative scan of
                                their state maps ([S], [G]) */
-  int32_t v_split;          /* 0 = choose; else 1, 2 or 4 workgroups per (seq, head)
-                               splitting the d_v columns of the state (fp32 inputs use
-                               at least 2) */
-  void *workspace;          /* device scratch of kda_prefill_workspace_size() bytes */
+  int32_t v_split;          /* 0 = choose (1); 1 or 2 workgroups per (seq, head)
+                               splitting the d_v columns of the state */
+  void *workspace;          /* device scratch of kda_prefill_workspace_size() bytes:
+                               per-chunk records (about 64.5 KB per chunk and head),
+                               plus segment maps and raw outputs when used */
   size_t workspace_bytes;
 } kda_prefill_desc;
 
@@ -129,7 +130,7 @@ KDA_API kda_status kda_prefill_workspace_size(const kda_prefill_desc *d, size_t 
 /* Enqueue the prefill.  Errors: NULL (q/k/v/g/beta/o, or ckpt when ckpt_every > 0,
  * or workspace when one is needed), SHAPE (negative sizes, ckpt_every not a
  * multiple of chunk, n_segments > number of chunks), UNSUPPORTED (d != 128, chunk
- * not 16/64, bad dtype, v_split not 0/1/2/4), WORKSPACE, ALIAS (o overlapping an
+ * not 16/64, bad dtype, v_split not 0/1/2), WORKSPACE, ALIAS (o overlapping an
  * input, or S_final overlapping an input other than S0), DEVICE, HIP. */
 KDA_API kda_status kda_prefill_chunked(const kda_prefill_desc *d, hipStream_t stream);
 

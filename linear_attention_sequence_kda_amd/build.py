@@ -21,7 +21,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 
-SOURCES = ["api.cpp", "decode.hip", "state_copy.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "decode.hip", "state_copy.hip", "prefill_prep.hip", "prefill_state.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

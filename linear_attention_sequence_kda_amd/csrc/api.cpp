@@ -55,26 +55,18 @@ kda_status plan_prefill(const kda_prefill_desc &d, PrefillPlan *p) {
   const int64_t units = static_cast<int64_t>(d.B) * d.H;
   p->n_chunks = static_cast<int>(n_chunks);
 
-  // columns per workgroup: split the value columns when (sequence, head) units alone
-  // fill at least a quarter of the chip; otherwise keep whole heads and split the
-  // sequence into segments (context parallelism), which does not repeat the
-  // per-token decay work in several workgroups
-  int vs = d.v_split;
-  if (vs == 0) {
-    if (units >= kTargetWorkgroups) vs = 1;
-    else if (units * 4 >= kTargetWorkgroups) vs = units * 2 >= kTargetWorkgroups ? 2 : 4;
-    else vs = 1;
-  }
-  if (d.in_dtype == KDA_F32 && vs < 2) vs = 2;   // fp32 operands: at most 64 columns per workgroup
+  // columns per workgroup: whole heads unless the caller asks for a split (a split
+  // head re-reads every chunk record once per workgroup and needs a separate norm
+  // pass); parallelism beyond the (sequence, head) units comes from segments
+  const int vs = d.v_split != 0 ? d.v_split : 1;
   p->v_split = vs;
 
-  // segments
+  // segments: context parallelism until the chip is covered, keeping >= 8 chunks each
   int64_t ns = d.n_segments;
   if (ns > 1 && ns > n_chunks) return KDA_ERR_SHAPE;
   if (ns == 0) {
     ns = 1;
-    // grow until the chip is covered, keeping >= 16 chunks per segment
-    while (units * vs * ns < kTargetWorkgroups && n_chunks / (ns * 2) >= 16) ns *= 2;
+    while (units * vs * ns < kTargetWorkgroups && n_chunks / (ns * 2) >= 8) ns *= 2;
   }
   if (ns < 1) ns = 1;
   int64_t seg_chunks = n_chunks > 0 ? (n_chunks + ns - 1) / ns : 0;
@@ -84,6 +76,8 @@ kda_status plan_prefill(const kda_prefill_desc &d, PrefillPlan *p) {
   p->split_norm = d.gate != nullptr && vs > 1;
 
   const size_t dkdv = static_cast<size_t>(d.d_k) * d.d_v;
+  p->ws_rec = static_cast<size_t>(units) * static_cast<size_t>(n_chunks) *
+              kda::prefill_record_bytes(d.chunk, d.in_dtype == KDA_F32);
   if (p->n_seg > 1) {
     p->ws_maps = static_cast<size_t>(units) * p->n_seg * dkdv * 2 * sizeof(float);
     p->ws_sin = static_cast<size_t>(units) * p->n_seg * dkdv * sizeof(float);
@@ -91,7 +85,11 @@ kda_status plan_prefill(const kda_prefill_desc &d, PrefillPlan *p) {
   if (p->split_norm && d.out_dtype == KDA_BF16)
     p->ws_norm = static_cast<size_t>(units) * static_cast<size_t>(d.T) * d.d_v * sizeof(float);
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  p->ws_total = up(p->ws_maps) + up(p->ws_sin) + up(p->ws_norm);
+  p->off_rec = 0;
+  p->off_maps = p->off_rec + up(p->ws_rec);
+  p->off_sin = p->off_maps + up(p->ws_maps);
+  p->off_norm = p->off_sin + up(p->ws_sin);
+  p->ws_total = p->off_norm + up(p->ws_norm);
   return KDA_OK;
 }
 
@@ -102,7 +100,7 @@ kda_status validate_sizes(const kda_prefill_desc *d) {
   if (d->chunk != 16 && d->chunk != 64) return KDA_ERR_UNSUPPORTED;
   if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return KDA_ERR_UNSUPPORTED;
   if (d->in_dtype == KDA_F32 && d->chunk != 16) return KDA_ERR_UNSUPPORTED;
-  if (d->v_split != 0 && d->v_split != 1 && d->v_split != 2 && d->v_split != 4)
+  if (d->v_split != 0 && d->v_split != 1 && d->v_split != 2)
     return KDA_ERR_UNSUPPORTED;
   if (d->n_segments < 0) return KDA_ERR_SHAPE;
   if (d->ckpt_every < 0 || (d->ckpt_every > 0 && d->ckpt_every % d->chunk != 0)) return KDA_ERR_SHAPE;

@@ -20,11 +20,19 @@ struct PrefillPlan {
   int n_chunks;     // chunks per sequence
   int v_split;      // workgroups per (sequence, head, segment) over the value columns
   bool split_norm;  // norm/gate epilogue runs as a separate pass (v_split > 1 with a gate)
+  size_t ws_rec;    // bytes: per-chunk records [B,H,n_chunks] written by the prep kernel
   size_t ws_maps;   // bytes: segment maps [B,H,n_seg,d_k,2*d_v] fp32
   size_t ws_sin;    // bytes: states entering each segment [B,H,n_seg,d_k,d_v] fp32
   size_t ws_norm;   // bytes: raw fp32 outputs [B,T,H,d_v] for the separate norm pass (bf16 out)
+  size_t off_rec, off_maps, off_sin, off_norm;   // byte offsets in the workspace
   size_t ws_total;
 };
+
+// Bytes of one per-chunk record (chunk 16 or 64; fp32 inputs use chunk 16).
+size_t prefill_record_bytes(int chunk, bool f32);
+
+// Pass 0 of the prefill: records of every (sequence, head, chunk).
+hipError_t launch_prefill_prep(const kda_prefill_desc &d, int n_chunks, void *records, hipStream_t s);
 
 hipError_t launch_prefill(const kda_prefill_desc &d, const PrefillPlan &p, hipStream_t s);
 

@@ -34,7 +34,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
-__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// 1 / (1 + e^-x) with the hardware exp2 and reciprocal (about 1 ulp each)
+__device__ __forceinline__ float sigmoidf_(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + exp2_fast(-x * kLog2e));
+}
 
 // Load 4 consecutive elements of a bf16 or fp32 array as floats (16/8-byte aligned).
 template <bool BF16>

@@ -1,0 +1,525 @@
+// Chunkwise KDA prefill, part 1: the per-chunk work that does not depend on the state.
+//
+// The sequence is cut into chunks; chunks are linked by the state recurrence and
+// computed inside with matrix products ("xhh.club" tag page 结构, entry on the chunkwise
+// algorithm).  For a chunk of C tokens, with G the inclusive cumulative sum of the
+// floored log-decay over the chunk (per key channel):
+//
+//   A  = StrictLower(diag(beta) (K e^G)(K e^-G)^T)      C x C   (decay-weighted K K^T)
+//   P  = Lower((Q e^G)(K e^-G)^T)                       C x C   (decay-weighted Q K^T)
+//   T  = (I + A)^-1 diag(beta)                          triangular solve (WY/UT form)
+//   W  = T (K e^G),   Qt = Q e^G,   Kdec = K e^{G_C - G},   decay = e^{G_C}
+//
+// None of these depends on the state entering the chunk, so every (sequence, head,
+// chunk) is prepared independently here, fully in parallel, and written to a record
+// (see Rec in tiles.h) that the sequential state kernel reads.
+//
+// Numerics ("xhh.club", chunkwise entry; "nlpx.cn" K3 guide section 6).  e^{+-G} over a
+// whole chunk over/underflows fp32, so A and P are formed on 16-token tiles with a
+// tile-local reference point r: for a diagonal tile the row factor e^{G_t - r} lies in
+// [e^-80, 1] and the column factor e^{r - G_j} in [1, e^80] only because every step's
+// log-decay is floored at -5 (16 * 5 = 80 < ln(FLT_MAX) = 88.7).  Those factors need a
+// wide exponent, so diagonal tiles run as BF16 MFMA, P's with each operand split into
+// bf16 high and low parts (three products).  In off-diagonal tiles both factors are
+// <= 1 and run as fp16 MFMA, as do the solve and W; all accumulation is fp32.  With
+// fp32 inputs every product runs as fp32 MFMA instead.
+#include <atomic>
+#include <utility>
+
+#include "internal.h"
+#include "tiles.h"
+
+namespace kda {
+namespace {
+
+struct PrepArgs {
+  const void *q, *k;
+  const float *g, *beta;
+  unsigned char *rec;     // n_recs records of Rec<C, F32>::bytes
+  int T, H, n_chunks;
+  int64_t n_recs;         // B * H * n_chunks
+};
+
+template <int C, bool F32>
+struct PrepLayout {
+  using T = typename Op<F32>::T;
+  static constexpr int NT = C / 16;
+  static constexpr int KC = C < 32 ? 32 : C;          // token contraction extent (zero padded)
+  static constexpr size_t E = sizeof(T);
+  static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
+  static constexpr int AOL = C + 8;                   // padded row of the off-diagonal A (fp16)
+  static constexpr int NFAC = NT > 2 ? (NT - 1) * (NT - 2) / 2 : 1;   // tile pairs w - s' >= 2
+  static constexpr size_t bKT = (size_t)KC * D * E;   // K e^G      [t][i]  (rows >= C zero)
+  static constexpr size_t bKF = (size_t)KC * D * E;   // KF [t][i] (rows >= C zero), then W [t][i]
+  static constexpr size_t bPt = (size_t)KC * C * E;   // P^T        [j][t]  (rows >= C zero)
+  static constexpr size_t bTt = (size_t)KC * C * E;   // T^T        [j][t]  (rows >= C zero)
+  static constexpr size_t bAd = (size_t)NT * 256 * 4; // diagonal blocks of A, fp32
+  static constexpr size_t bAo = NT > 1 ? (size_t)C * AOL * 2 : 0;   // A, off-diagonal blocks
+  static constexpr size_t bX = (size_t)NT * 256 * 4;  // inverses of the diagonal blocks of I + A
+  static constexpr size_t oKT = 0;
+  static constexpr size_t oKF = al(oKT + bKT);
+  static constexpr size_t oPt = al(oKF + bKF);
+  static constexpr size_t oTt = al(oPt + bPt);
+  static constexpr size_t oAd = al(oTt + bTt);
+  static constexpr size_t oAo = al(oAd + bAd);
+  static constexpr size_t oX = al(oAo + bAo);
+  static constexpr size_t oDpow = al(oX + bX);                  // D_m = e^{tile m total}
+  static constexpr size_t oPre = oDpow + (size_t)NT * D * 4;    // prod_{m<w} D_m
+  static constexpr size_t oPost = oPre + (size_t)NT * D * 4;    // prod_{m>w} D_m
+  static constexpr size_t oFac = oPost + (size_t)NT * D * 4;    // prod_{s'<m<w} D_m
+  static constexpr size_t oBeta = oFac + (size_t)NFAC * D * 4;
+  static constexpr size_t oDecay = oBeta + (size_t)KC * 4;
+  static constexpr size_t bytes = al(oDecay + D * 4);
+};
+
+// Raw inputs of one chunk held in registers between the load and their use.
+template <bool F32>
+struct RawPrep {
+  float4 g[8];          // log-decay of this lane's token: g[2kb] channels 32kb + 4lg + (0..3),
+                        // g[2kb + 1] channels 32kb + 16 + 4lg + (0..3)
+  Q8<F32> k[4], q[4];
+  float beta;
+};
+
+// Global loads of one chunk, zero-filled past the sequence end.  Wave w < NT loads
+// token tile w: lane (lr, lg) gets token 16w + lr and, per 32-channel block kb, the
+// channels of the split contraction order, 32kb + 4lg + (0..3) and 32kb + 16 + 4lg +
+// (0..3) (see ld_n_split): every operand built from them is already in that order.
+template <int C, bool F32>
+__device__ __forceinline__ void load_prep(RawPrep<F32> &r, const PrepArgs &a, int64_t rec, int tid) {
+  constexpr int NT = C / 16;
+  const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+  const int bh = (int)(rec / a.n_chunks), chunk = (int)(rec % a.n_chunks);
+  const int b = bh / a.H, h = bh % a.H;
+  const int t0 = chunk * C;
+  const int tt = 16 * wave + lr;
+  const bool ok = wave < NT && t0 + tt < a.T;
+  const size_t tok = (size_t)b * a.T + t0 + tt;
+  const size_t base = (tok * a.H + h) * D + 4 * lg;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    if (ok) {
+      r.g[2 * kb] = *reinterpret_cast<const float4 *>(a.g + base + 32 * kb);
+      r.g[2 * kb + 1] = *reinterpret_cast<const float4 *>(a.g + base + 32 * kb + 16);
+      r.k[kb] = load_q8_split<F32>(a.k, base + 32 * kb);
+      r.q[kb] = load_q8_split<F32>(a.q, base + 32 * kb);
+    } else {
+      r.g[2 * kb] = r.g[2 * kb + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      r.k[kb] = zero_q8<F32>();
+      r.q[kb] = zero_q8<F32>();
+    }
+  }
+  r.beta = ok ? a.beta[tok * a.H + h] : 0.f;
+}
+
+// one step of the 16-lane inclusive scan on 8 independent values (DPP row shift right)
+template <int CTRL>
+__device__ __forceinline__ void scan_step(float *x) {
+  float sv[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    sv[e] = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x[e]), CTRL, 0xf, 0xf, false));
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] += sv[e];
+}
+
+// Column j of the inverse of a unit lower triangular 16x16 block I + A by forward
+// substitution, x_i = [i == j] - sum_{m<i} A[i][m] x_m.  Lane j of each 16-lane row
+// holds row j of its block's A in rowA; A[i][m] is broadcast from lane i of the row.
+template <int I>
+__device__ __forceinline__ void invert_row(const float *rowA, float *x, int j) {
+  float acc = 0.f;
+#pragma unroll
+  for (int m = 0; m < I; ++m) {
+    const float a = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, rowA[m]), 0x150 + I, 0xf, 0xf, false));
+    acc = fmaf(a, x[m], acc);
+  }
+  x[I] = (I == j ? 1.f : 0.f) - acc;
+  __builtin_amdgcn_sched_barrier(0);   // keep the broadcasts of later rows from being hoisted
+}
+
+template <int... Is>
+__device__ __forceinline__ void invert_unit_lower(const float *rowA, float *x, int j, std::integer_sequence<int, Is...>) {
+  (invert_row<Is>(rowA, x, j), ...);
+}
+
+template <int C, bool F32>
+__global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepArgs a) {
+  using L = PrepLayout<C, F32>;
+  using R = Rec<C, F32>;
+  using T = typename Op<F32>::T;
+  using V8 = typename Op<F32>::V8;
+  constexpr int NT = L::NT, KC = L::KC, KB = R::KB;
+  static_assert(!F32 || C == 16, "fp32 operands are used with 16-token chunks only");
+  extern __shared__ __align__(16) unsigned char smem[];
+  T *sKT = reinterpret_cast<T *>(smem + L::oKT);       // rows of D
+  T *sKF = reinterpret_cast<T *>(smem + L::oKF);       // rows of D
+  T *sW = sKF;                                         // W [t][i], after KF is dead
+  T *sPt = reinterpret_cast<T *>(smem + L::oPt);       // rows of C
+  T *sTt = reinterpret_cast<T *>(smem + L::oTt);       // rows of C
+  float *sAd = reinterpret_cast<float *>(smem + L::oAd);
+  _Float16 *sAo = reinterpret_cast<_Float16 *>(smem + L::oAo);
+  float *sX = reinterpret_cast<float *>(smem + L::oX);
+  float *sDpow = reinterpret_cast<float *>(smem + L::oDpow);
+  float *sPre = reinterpret_cast<float *>(smem + L::oPre);
+  float *sPost = reinterpret_cast<float *>(smem + L::oPost);
+  float *sFac = reinterpret_cast<float *>(smem + L::oFac);
+  float *sBeta = reinterpret_cast<float *>(smem + L::oBeta);
+  float *sDecay = reinterpret_cast<float *>(smem + L::oDecay);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int tt = 16 * wave + lr;                       // this lane's token in phase A
+
+  // zero the padded token range of the contraction buffers once (only when KC > C)
+  if constexpr (KC > C) {
+    for (int x = tid; x < (KC - C) * D; x += NTHREADS) { sKT[C * D + x] = T(0); sKF[C * D + x] = T(0); }
+    for (int x = tid; x < (KC - C) * C; x += NTHREADS) { sPt[C * C + x] = T(0); sTt[C * C + x] = T(0); }
+  }
+
+  const int64_t rec = blockIdx.x;
+  if (rec >= a.n_recs) return;
+  RawPrep<F32> raw;
+  load_prep<C, F32>(raw, a, rec, tid);
+  {
+    unsigned char *out = a.rec + (size_t)rec * R::bytes;
+
+    // ===== A1: tile-relative cumulative log2-decay; tile totals; beta =====
+    float Lc[32];
+    if (wave < NT) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int ch = 32 * kb + 4 * lg;               // channels ch + (0..3), ch + 16 + (0..3)
+        float gg[8];
+        f8_from(gg, raw.g[2 * kb], raw.g[2 * kb + 1]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Lc[8 * kb + e] = log2_decay(gg[e]);
+        scan_step<0x111>(Lc + 8 * kb);
+        scan_step<0x112>(Lc + 8 * kb);
+        scan_step<0x114>(Lc + 8 * kb);
+        scan_step<0x118>(Lc + 8 * kb);
+        if (lr == 15) {                                  // tile decays D_w = e^{tile total}
+          float dp[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dp[e] = exp2_fast(Lc[8 * kb + e]);
+          float *pp = sDpow + wave * D + ch;
+          *reinterpret_cast<float4 *>(pp) = make_float4(dp[0], dp[1], dp[2], dp[3]);
+          *reinterpret_cast<float4 *>(pp + 16) = make_float4(dp[4], dp[5], dp[6], dp[7]);
+        }
+      }
+      if (lg == 0) sBeta[tt] = raw.beta;
+    }
+    __syncthreads();
+
+    // ===== per (tile, channel): prefix and suffix decay products, the chunk decay,
+    // and the factors between tiles two or more apart =====
+    if constexpr (NT > 1) {
+      const int ch = tid & (D - 1), half = tid >> 7;
+      float dp[NT];
+#pragma unroll
+      for (int m = 0; m < NT; ++m) dp[m] = sDpow[m * D + ch];
+      if (half == 0) {
+        float p = 1.f;
+#pragma unroll
+        for (int m = 0; m < NT; ++m) { sPre[m * D + ch] = p; p *= dp[m]; }
+        sDecay[ch] = p;
+        int pi = 0;
+#pragma unroll
+        for (int w = 2; w < NT; ++w)
+#pragma unroll
+          for (int sp = 0; sp + 2 <= w; ++sp) {
+            float f = 1.f;
+#pragma unroll
+            for (int m = sp + 1; m < w; ++m) f *= dp[m];
+            sFac[pi * D + ch] = f;
+            ++pi;
+          }
+      } else {
+        float p = 1.f;
+#pragma unroll
+        for (int m = NT - 1; m >= 0; --m) { sPost[m * D + ch] = p; p *= dp[m]; }
+      }
+    } else {
+      if (tid < D) { sPre[tid] = 1.f; sPost[tid] = 1.f; sDecay[tid] = sDpow[tid]; }
+    }
+    __syncthreads();
+
+    // ===== A2: decay factors, diagonal tile, chunk-level operands =====
+    V8 rkx[4], rqx[4];                                 // k e^{G_t - r_w}, q e^{G_t - r_w}
+    if (wave < NT) {
+      f32x4 accAd = zero4(), accPd = zero4();          // diagonal tile (w, w)
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int ch = 32 * kb + 4 * lg;               // channels ch + (0..3), ch + 16 + (0..3)
+        float pre[8], dw[8];
+        f8_from(pre, *reinterpret_cast<const float4 *>(sPre + wave * D + ch),
+                *reinterpret_cast<const float4 *>(sPre + wave * D + ch + 16));
+        f8_from(dw, *reinterpret_cast<const float4 *>(sDpow + wave * D + ch),
+                *reinterpret_cast<const float4 *>(sDpow + wave * D + ch + 16));
+        float rk[8], rq[8], yd[8], xk[8], xf[8];
+        V8 xq;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float Lv = Lc[8 * kb + e], kk = q8_at<F32>(raw.k[kb], e), qq = q8_at<F32>(raw.q[kb], e);
+          const float E = exp2_fast(Lv);               // e^{G_t - r_w}      in [e^-80, 1]
+          const float En = exp2_fast(-Lv);             // e^{r_w - G_t}      in [1, e^80]
+          rk[e] = kk * E;
+          rq[e] = qq * E;
+          yd[e] = kk * En;                             // k e^{r_w - G_t}
+          xf[e] = yd[e] * dw[e];                       // k e^{r_{w+1} - G_t}, in [e^-75, 1] |k|
+          xq[e] = Op<F32>::cvt(rq[e] * pre[e]);        // q e^{G_t}
+          xk[e] = rk[e] * pre[e];                      // k e^{G_t}
+          rkx[kb][e] = Op<F32>::cvt(rk[e]);            // kept for the off-diagonal tiles
+          rqx[kb][e] = Op<F32>::cvt(rq[e]);
+        }
+        // Qt goes out directly: this lane layout is the operand fragment (tile w, kb)
+        Op<F32>::store(reinterpret_cast<T *>(out + R::frag(R::oQ, wave * 4 + kb, lane)), xq);
+        st4<F32, D>(sKT, tt, ch, xk[0], xk[1], xk[2], xk[3]);
+        st4<F32, D>(sKT, tt, ch + 16, xk[4], xk[5], xk[6], xk[7]);
+        st4<F32, D>(sKF, tt, ch, xf[0], xf[1], xf[2], xf[3]);
+        st4<F32, D>(sKF, tt, ch + 16, xf[4], xf[5], xf[6], xf[7]);
+        // diagonal tile (w, w) straight from registers: A in bf16, P with bf16 hi/lo
+        if constexpr (F32) {
+          const V8 va{rk[0], rk[1], rk[2], rk[3], rk[4], rk[5], rk[6], rk[7]};
+          const V8 vq{rq[0], rq[1], rq[2], rq[3], rq[4], rq[5], rq[6], rq[7]};
+          const V8 vy{yd[0], yd[1], yd[2], yd[3], yd[4], yd[5], yd[6], yd[7]};
+          accAd = Op<true>::mma(accAd, va, vy);
+          accPd = Op<true>::mma(accPd, vq, vy);
+        } else {
+          bf16x8 kh, yh, qh, ql, yl;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            kh[e] = static_cast<__bf16>(rk[e]);
+            yh[e] = static_cast<__bf16>(yd[e]);
+            qh[e] = static_cast<__bf16>(rq[e]);
+            ql[e] = static_cast<__bf16>(rq[e] - static_cast<float>(qh[e]));
+            yl[e] = static_cast<__bf16>(yd[e] - static_cast<float>(yh[e]));
+          }
+          accAd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, yh, accAd, 0, 0, 0);
+          accPd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, yh, accPd, 0, 0, 0);
+          accPd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, yl, accPd, 0, 0, 0);
+          accPd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, yh, accPd, 0, 0, 0);
+        }
+      }
+      // diagonal tile: A (beta rows, strictly lower, fp32), P^T (lower incl.), and
+      // P's zero blocks above the diagonal of this tile row
+      float pv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int ti = 4 * lg + r, t = 16 * wave + ti;
+        sAd[wave * 256 + ti * 16 + lr] = ti > lr ? accAd[r] * sBeta[t] : 0.f;
+        pv[r] = ti >= lr ? accPd[r] : 0.f;
+      }
+      st4<F32, C>(sPt, 16 * wave + lr, 16 * wave + 4 * lg, pv[0], pv[1], pv[2], pv[3]);
+#pragma unroll
+      for (int sp = 1; sp < NT; ++sp)
+        if (sp > wave) st4<F32, C>(sPt, 16 * sp + lr, 16 * wave + 4 * lg, 0.f, 0.f, 0.f, 0.f);
+    }
+    __syncthreads();   // KF, Kt, decay, diagonal A/P visible
+
+    // ===== A3: wave 0 inverts every diagonal block of I + A (one column per lane);
+    // waves w >= 1 compute the off-diagonal tiles (w, s'), s' < w, with row operand
+    // k e^{G_t - r_w} prod_{s'<m<w} D_m and column operand KF of tile s' (both <= 1) ====
+    if (wave == 0) {
+      const int bb = lane >> 4, j = lane & 15;
+      float rowA[16], x[16];
+      if (bb < NT) {
+#pragma unroll
+        for (int m4 = 0; m4 < 4; ++m4) {
+          const float4 v = *reinterpret_cast<const float4 *>(sAd + bb * 256 + j * 16 + 4 * m4);
+          rowA[4 * m4] = v.x; rowA[4 * m4 + 1] = v.y; rowA[4 * m4 + 2] = v.z; rowA[4 * m4 + 3] = v.w;
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 16; ++m) rowA[m] = 0.f;
+      }
+      invert_unit_lower(rowA, x, j, std::make_integer_sequence<int, 16>{});
+      if (bb < NT) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sX[bb * 256 + i * 16 + j] = x[i];
+      }
+    } else if (wave < NT) {
+      f32x4 accA[NT], accP[NT];
+#pragma unroll
+      for (int sp = 0; sp < NT; ++sp) { accA[sp] = zero4(); accP[sp] = zero4(); }
+#pragma unroll
+      for (int sp = 0; sp < NT - 1; ++sp) {
+        if (sp < wave) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const int ch = 32 * kb + 4 * lg;
+            V8 va = rkx[kb], vq = rqx[kb];
+            if (sp + 1 < wave) {                         // tiles two or more apart: scale by
+              const int pi = (wave - 2) * (wave - 1) / 2 + sp;   // prod_{s'<m<w} D_m
+              float fac[8];
+              f8_from(fac, *reinterpret_cast<const float4 *>(sFac + pi * D + ch),
+                      *reinterpret_cast<const float4 *>(sFac + pi * D + ch + 16));
+              V8 vf;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) vf[e] = Op<F32>::cvt(fac[e]);
+              va = va * vf;
+              vq = vq * vf;
+            }
+            const V8 vb = ld_n_split<F32, D>(sKF, 16 * sp, 32 * kb, lane);
+            accA[sp] = Op<F32>::mma(accA[sp], va, vb);
+            accP[sp] = Op<F32>::mma(accP[sp], vq, vb);
+          }
+        }
+      }
+#pragma unroll
+      for (int sp = 0; sp < NT - 1; ++sp) {
+        if (sp < wave) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * wave + 4 * lg + r;
+            sAo[t * L::AOL + 16 * sp + lr] = static_cast<_Float16>(accA[sp][r] * sBeta[t]);
+          }
+          st4<F32, C>(sPt, 16 * sp + lr, 16 * wave + 4 * lg, accP[sp][0], accP[sp][1], accP[sp][2], accP[sp][3]);
+        }
+      }
+    }
+    // Kdec^T fragments: Kdec = KF * prod_{m>w} D_m, read transposed from KF.  Lane
+    // (lr, lg) of fragment (ib, kb) holds channel 16ib + lr of tokens 32kb + 4lg + e
+    // (tile 2kb) and 32kb + 16 + 4lg + e (tile 2kb + 1).
+    for (int f = wave; f < R::nK; f += 4) {
+      const int ib = f / KB, kb = f % KB;
+      const float post0 = sPost[(2 * kb) * D + 16 * ib + lr];
+      const float post1 = 2 * kb + 1 < NT ? sPost[(2 * kb + 1) * D + 16 * ib + lr] : 0.f;
+      V8 v = ld_t_split<F32, D>(sKF, 32 * kb, 16 * ib, lane);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[e] = Op<F32>::cvt(static_cast<float>(v[e]) * (e < 4 ? post0 : post1));
+      Op<F32>::store(reinterpret_cast<T *>(out + R::frag(R::oK, f, lane)), v);
+    }
+    __syncthreads();   // A, P, diagonal inverses complete; KF dead
+
+    // ===== solve: wave w walks down column block w of X = (I + A)^-1:
+    // X_{s,w} = -X_ss sum_{w<=m<s} A_{s,m} X_{m,w}; a 16x16 result in MFMA output layout
+    // is the B operand layout of the K=16 MFMA, so the blocks stay in registers.
+    // Then T[:, block w] = X[:, block w] diag(beta), stored as T^T [j][t]. =====
+    if (wave < NT) {
+      const int n = lr;                                 // column within the block
+      const float bj = sBeta[16 * wave + n];
+      f32x4 xc[NT];
+#pragma unroll
+      for (int s = 0; s < NT; ++s) {
+        if (s == wave) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xc[s][r] = sX[wave * 256 + (4 * lg + r) * 16 + n];
+        } else {
+          xc[s] = zero4();
+        }
+      }
+      if constexpr (NT > 1 && !F32) {
+#pragma unroll
+        for (int s = 1; s < NT; ++s) {
+          if (s > wave) {
+            f32x4 y = zero4();
+#pragma unroll
+            for (int m = 0; m < NT - 1; ++m) {
+              if (m >= wave && m < s) {
+                const f16x4 a4 = *reinterpret_cast<const f16x4 *>(sAo + (16 * s + lr) * L::AOL + 16 * m + 4 * lg);
+                const f16x4 b4{(_Float16)xc[m][0], (_Float16)xc[m][1], (_Float16)xc[m][2], (_Float16)xc[m][3]};
+                y = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, b4, y, 0, 0, 0);
+              }
+            }
+            const float4 xv = *reinterpret_cast<const float4 *>(sX + s * 256 + lr * 16 + 4 * lg);
+            const f16x4 a4{(_Float16)xv.x, (_Float16)xv.y, (_Float16)xv.z, (_Float16)xv.w};
+            const f16x4 b4{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
+            const f32x4 z = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, b4, zero4(), 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) xc[s][r] = -z[r];
+          }
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < NT; ++s) {
+        const bool on = s >= wave;
+        st4<F32, C>(sTt, 16 * wave + n, 16 * s + 4 * lg, on ? xc[s][0] * bj : 0.f, on ? xc[s][1] * bj : 0.f,
+                    on ? xc[s][2] * bj : 0.f, on ? xc[s][3] * bj : 0.f);
+      }
+    }
+    __syncthreads();   // T complete
+
+    // ===== W^T = Kt^T T^T  ->  W [t][i] (over KF) =====
+    {
+      constexpr int NTILE = 8 * NT;                    // (i-block, t-block)
+#pragma unroll 2
+      for (int it = 0; it < (NTILE + 3) / 4; ++it) {
+        const int tile = wave + 4 * it;
+        if (tile < NTILE) {
+          const int ib = tile / NT, tb = tile % NT;
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+            acc = Op<F32>::mma(acc, ld_t<F32, D>(sKT, 32 * kb, 16 * ib, lane),
+                               ld_t<F32, C>(sTt, 32 * kb, 16 * tb, lane));
+          // acc[r] = W^T[16ib + 4lg + r][16tb + lr]
+          st4<F32, D>(sW, 16 * tb + lr, 16 * ib + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
+        }
+      }
+    }
+    __syncthreads();   // W complete
+
+    // ===== export W, P, T fragments and the chunk decay =====
+    constexpr int NEXP = R::nW + R::nP + R::nT;
+    for (int f = wave; f < NEXP; f += 4) {
+      V8 v;
+      size_t off;
+      if (f < R::nW) {
+        v = ld_n_split<F32, D>(sW, 16 * (f / 4), 32 * (f % 4), lane);
+        off = R::frag(R::oW, f, lane);
+      } else if (f < R::nW + R::nP) {
+        const int g = f - R::nW;
+        v = ld_t_split<F32, C>(sPt, 32 * (g % KB), 16 * (g / KB), lane);
+        off = R::frag(R::oP, g, lane);
+      } else {
+        const int g = f - R::nW - R::nP;
+        v = ld_t_split<F32, C>(sTt, 32 * (g % KB), 16 * (g / KB), lane);
+        off = R::frag(R::oT, g, lane);
+      }
+      Op<F32>::store(reinterpret_cast<T *>(out + off), v);
+    }
+    if (tid < D / 4)
+      reinterpret_cast<float4 *>(out + R::oDec)[tid] = reinterpret_cast<const float4 *>(sDecay)[tid];
+  }
+}
+
+template <int C, bool F32>
+hipError_t launch_prep_t(const PrepArgs &a, hipStream_t s) {
+  using L = PrepLayout<C, F32>;
+  static_assert(L::bytes <= 80 * 1024, "two workgroups per CU must fit in LDS");
+  auto kern = chunk_prep_kernel<C, F32>;
+  static std::atomic<bool> attr_set{false};   // the attribute is per function, set once
+  if (!attr_set.load(std::memory_order_acquire)) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)L::bytes);
+    if (e != hipSuccess) return e;
+    attr_set.store(true, std::memory_order_release);
+  }
+  // one workgroup per record; several resident per CU overlap one's loads with
+  // another's arithmetic
+  hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(a.n_recs)), dim3(NTHREADS), L::bytes, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t prefill_record_bytes(int chunk, bool f32) {
+  if (f32) return Rec<16, true>::bytes;
+  return chunk == 16 ? Rec<16, false>::bytes : Rec<64, false>::bytes;
+}
+
+hipError_t launch_prefill_prep(const kda_prefill_desc &d, int n_chunks, void *records, hipStream_t s) {
+  PrepArgs a{};
+  a.q = d.q; a.k = d.k; a.g = d.g; a.beta = d.beta;
+  a.rec = static_cast<unsigned char *>(records);
+  a.T = d.T; a.H = d.H; a.n_chunks = n_chunks;
+  a.n_recs = (int64_t)d.B * d.H * n_chunks;
+  if (a.n_recs == 0) return hipSuccess;
+  if (d.in_dtype == KDA_F32) return launch_prep_t<16, true>(a, s);
+  if (d.chunk == 16) return launch_prep_t<16, false>(a, s);
+  return launch_prep_t<64, false>(a, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,684 @@
+// Chunkwise KDA prefill, part 2: the state recurrence between chunks.
+//
+// Per chunk, with the record written by the prep kernel (W, Qt, P, T, Kdec, e^{G_C};
+// see prefill_prep.hip) and the state S (d_k x d_v) entering the chunk
+// ("xhh.club" tag page 结构, entry on the chunkwise algorithm: recurrence between
+// chunks, matrix products inside them):
+//
+//   U  = T V - W S                    the per-token writes u_t of the delta rule
+//   O  = Qt S + P U                   outputs (then the optional per-head RMSNorm and
+//                                     sigmoid gate, same page, entry on KDA's form)
+//   S <- Diag(e^{G_C}) S + Kdec^T U
+//
+// Value columns are independent in all three products, so each wave owns NC/4
+// columns of the state and runs its own recurrence on them: S and U stay in MFMA
+// accumulators and feed the next products straight from registers (the record's
+// operands are stored with the contraction index in the matching split order).  The
+// only data shared by the waves of a workgroup is the chunk's record, which is
+// copied into LDS once per workgroup by asynchronous global->LDS loads, one chunk
+// ahead (two buffers), and the chunk's values V.  All products are fp16 MFMA with
+// fp32 accumulation (fp32 MFMA for fp32 inputs).  MODE_TRANSITION computes a
+// segment's state map for the associative scan of context parallelism instead of
+// outputs.
+#include <type_traits>
+
+#include "internal.h"
+#include "tiles.h"
+
+namespace kda {
+namespace {
+
+constexpr int MODE_OUTPUT = 0;
+constexpr int MODE_TRANSITION = 1;
+
+struct StateArgs {
+  const void *v, *gate;
+  const float *S0, *norm_weight;
+  const unsigned char *rec;   // prep records, [B*H][n_chunks]
+  float *S_final, *ckpt;
+  void *o;
+  float *maps;        // [units][D][2D] segment maps (transition mode)
+  const float *sin;   // [units][D][D] states entering each segment (segmented output mode)
+  float eps;
+  int T, H;
+  int n_seg, seg_chunks, n_chunks;
+  int ckpt_every, n_ckpt;
+  int out_bf16, fused_gate, raw_out;   // raw_out: write raw fp32 o for a separate norm pass
+  int n_units;        // B * H * n_seg
+};
+
+// value columns of one chunk for this workgroup's slice: groups of 8 columns, token-major
+template <int C, int NC, bool F32>
+struct VRaw {
+  static constexpr int NVG = C * NC / 8;
+  static constexpr int NVPT = (NVG + NTHREADS - 1) / NTHREADS;
+  Q8<F32> v[NVPT];
+};
+
+// x where ok, else zeros, without a branch
+template <bool F32>
+__device__ __forceinline__ Q8<F32> keep_if(Q8<F32> x, bool ok) {
+  const uint32_t m = ok ? 0xffffffffu : 0u;
+  if constexpr (F32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = __uint_as_float(__float_as_uint(x[e]) & m);
+    return x;
+  } else {
+    return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+  }
+}
+
+// Branch-free loads with addresses clamped into the chunk; values past the chunk (and
+// the A part of a transition map, which carries no value) are zeroed when stored to
+// LDS, so that a load is never consumed right after it is issued.
+template <int C, int NC, bool F32, int MODE>
+__device__ __forceinline__ void load_v(VRaw<C, NC, F32> &r, const StateArgs &a, size_t tok0, int nval,
+                                       int c0, int tid) {
+  using VR = VRaw<C, NC, F32>;
+  constexpr int per_tok = NC / 8;
+  const size_t tok_stride = (size_t)a.H * D;
+  const int cv = MODE == MODE_OUTPUT ? c0 : max(c0 - D, 0);
+#pragma unroll
+  for (int u = 0; u < VR::NVPT; ++u) {
+    const int x = tid + u * NTHREADS;
+    const int tc = min(x / per_tok, nval - 1);
+    r.v[u] = load_q8<F32>(a.v, tok0 + (size_t)tc * tok_stride + cv + (x % per_tok) * 8);
+  }
+}
+
+template <int C, int NC, bool F32, int MODE>
+__device__ __forceinline__ void store_v(typename Op<F32>::T *sV, const VRaw<C, NC, F32> &r, int nval, int c0,
+                                        int tid) {
+  using VR = VRaw<C, NC, F32>;
+  constexpr int per_tok = NC / 8;
+  // transition mode: virtual columns < D form the A part of the map and carry no value
+  const bool has_v = MODE == MODE_OUTPUT || c0 >= D;
+#pragma unroll
+  for (int u = 0; u < VR::NVPT; ++u) {
+    const int x = tid + u * NTHREADS;
+    if (VR::NVG % NTHREADS == 0 || x < VR::NVG) {
+      const Q8<F32> q = keep_if<F32>(r.v[u], has_v && x / per_tok < nval);
+      float vv[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vv[e] = q8_at<F32>(q, e);
+      st8<F32, NC>(sV, x / per_tok, (x % per_tok) * 8, vv);
+    }
+  }
+}
+
+// 4 consecutive inputs of a bf16 or fp32 tensor
+template <bool F32>
+using Q4 = typename std::conditional<F32, float4, uint2>::type;
+
+template <bool F32>
+__device__ __forceinline__ Q4<F32> load_q4(const void *p, size_t idx) {
+  if constexpr (F32) return *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + idx);
+  else return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + idx);
+}
+
+template <bool F32>
+__device__ __forceinline__ float q4_at(const Q4<F32> &x, int e) {
+  if constexpr (F32) {
+    return e == 0 ? x.x : e == 1 ? x.y : e == 2 ? x.z : x.w;
+  } else {
+    const uint32_t w = e < 2 ? x.x : x.y;
+    return __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+  }
+}
+
+// GATE: the output pass of a whole head (NC = 128) with the fused RMSNorm and gate
+template <int C, int NC, bool F32, int MODE, bool GATE>
+__global__ __launch_bounds__(NTHREADS, 1) void chunk_state_kernel(StateArgs a) {
+  using R = Rec<C, F32>;
+  using T = typename Op<F32>::T;
+  using V8 = typename Op<F32>::V8;
+  constexpr int KC = C < 32 ? 32 : C;
+  constexpr int KB = R::KB, NT = C / 16;
+  constexpr int NCW = NC / 4;                          // state columns per wave
+  constexpr int CBW = NCW / 16;                        // 16-column blocks per wave
+  static_assert(CBW >= 1, "each wave owns at least one 16-column block");
+  static_assert(!GATE || (MODE == MODE_OUTPUT && NC == D), "the fused epilogue needs whole heads");
+  constexpr int VS = (MODE == MODE_TRANSITION ? 2 * D : D) / NC;   // workgroups per unit
+  constexpr int NBLK = (int)(R::bytes / 1024);         // record size in KiB
+  // Two record buffers, the chunk's values and the norm partials are separate LDS
+  // objects, so the compiler sees that reads of one buffer do not depend on the
+  // asynchronous copy in flight into the other.
+  __shared__ __align__(16) unsigned char recA[R::bytes];
+  __shared__ __align__(16) unsigned char recB[R::bytes];
+  __shared__ __align__(16) T sV[KC * NC];              // V [t][c] (rows >= C zero)
+  __shared__ float sNorm[GATE ? 4 * C : 1];            // per-wave sums of squares
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+
+  // XCD-aware placement: consecutive workgroup ids go to different XCDs, so the
+  // column slices of one unit get ids that are equal modulo 8 (same XCD, shared L2
+  // for the record they both read).
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, rest = bid >> 3;
+  const int slice = rest % VS;
+  const int unit = (rest / VS) * 8 + xcd;
+  if (unit >= a.n_units) return;
+  const int seg = unit % a.n_seg;
+  if (MODE == MODE_TRANSITION && seg == a.n_seg - 1) return;   // last map is never used
+  const int bh = unit / a.n_seg;
+  const int h = bh % a.H, b = bh / a.H;
+  const int c0 = slice * NC;                           // first (virtual) column of this slice
+  const int cw = wave * NCW;                           // this wave's first column in the slice
+  const size_t tok_stride = (size_t)a.H * D;
+  const size_t state_off = (size_t)bh * D * D;
+  const unsigned char *rec_bh = a.rec + (size_t)bh * a.n_chunks * R::bytes;
+  auto tok_base = [&](int chunk) __attribute__((always_inline)) {
+    return ((size_t)b * a.T + (size_t)chunk * C) * tok_stride + (size_t)h * D;
+  };
+
+  // V rows past the chunk stay zero (only when KC > C)
+  if constexpr (KC > C) {
+    for (int x = tid; x < (KC - C) * NC; x += NTHREADS) sV[C * NC + x] = T(0);
+  }
+
+  // ---- initial state: S[ib][j] holds rows 16ib + 4lg + r, column c0 + cw + 16j + lr
+  f32x4 S[8][CBW];
+#pragma unroll
+  for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      const int c = c0 + cw + 16 * j + lr;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = 16 * ib + 4 * lg + r;
+        float x;
+        if constexpr (MODE == MODE_TRANSITION) {
+          x = (c < D && i == c) ? 1.f : 0.f;           // [A | B] starts at [I | 0]
+        } else if (a.n_seg > 1) {
+          x = a.sin[(size_t)unit * D * D + (size_t)i * D + c];   // from the segment scan
+        } else {
+          x = a.S0 ? a.S0[state_off + (size_t)i * D + c] : 0.f;
+        }
+        S[ib][j][r] = x;
+      }
+    }
+
+  // asynchronous copy of one chunk's record into an LDS buffer: one KiB per wave
+  // instruction, lane l's 16 bytes landing at offset 16 l of that KiB (every wave
+  // issues the same number of copies, the last KiB possibly twice, so the count of
+  // memory operations in flight is known at compile time)
+  constexpr int NCOPY = (NBLK + 3) / 4;                // copies per wave and chunk
+  auto copy_rec = [&](unsigned char *dst, int chunk, int n0, int n1) __attribute__((always_inline)) {
+    const unsigned char *src = rec_bh + (size_t)chunk * R::bytes + 16 * lane;
+#pragma unroll
+    for (int n = n0; n < n1; ++n) {
+      const int blk = min(wave + 4 * n, NBLK - 1);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + (size_t)blk * 1024),
+                                       (__attribute__((address_space(3))) void *)(dst + (size_t)blk * 1024), 16, 0, 0);
+    }
+  };
+  // gate logits for the fused epilogue: token 16tb + lr, columns cw + 16j + 4lg .. +3
+  auto load_gate = [&](Q4<F32> (&gt)[NT][CBW], int chunk) __attribute__((always_inline)) {
+    const int nv = min(C, a.T - chunk * C);
+    const size_t base = tok_base(chunk) + cw + 4 * lg;
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb)
+#pragma unroll
+      for (int j = 0; j < CBW; ++j) {
+        const int t = min(16 * tb + lr, nv - 1);   // rows past the end are never used
+        gt[tb][j] = load_q4<F32>(a.gate, base + (size_t)t * tok_stride + 16 * j);
+      }
+  };
+
+  const int ch_begin = seg * a.seg_chunks;
+  const int ch_end = min(a.n_chunks, ch_begin + a.seg_chunks);
+
+  // Pipeline.  Within one chunk no register loaded during that chunk is consumed:
+  // with loads, stores and LDS copies in flight together the compiler can only wait
+  // for all of them, so every wait happens at the top of a chunk, where the record
+  // copy has to be complete anyway.  Per chunk n: the record of n+1 is copied, the
+  // gate of n+1 is loaded, the outputs of n-1 are stored, and in the middle of the
+  // chunk the values of n+1 (loaded during n-1) go to LDS and those of n+2 are loaded.
+  VRaw<C, NC, F32> vr;
+  Q4<F32> gc[NT][CBW], gn[NT][CBW];
+  f32x4 op[NT][CBW];                                   // outputs of the previous chunk
+  float wv[CBW][4];                                    // RMSNorm weights of this wave's columns
+  if constexpr (GATE) {
+#pragma unroll
+    for (int j = 0; j < CBW; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) wv[j][r] = a.norm_weight ? a.norm_weight[cw + 16 * j + 4 * lg + r] : 1.f;
+  }
+  const int ch_last = ch_end - 1;
+  load_v<C, NC, F32, MODE>(vr, a, tok_base(ch_begin), min(C, a.T - ch_begin * C), c0, tid);
+  if constexpr (GATE) load_gate(gn, ch_begin);
+  copy_rec(recA, ch_begin, 0, NCOPY);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  store_v<C, NC, F32, MODE>(sV, vr, min(C, a.T - ch_begin * C), c0, tid);
+  {
+    const int n1 = min(ch_begin + 1, ch_last);
+    load_v<C, NC, F32, MODE>(vr, a, tok_base(n1), min(C, a.T - n1 * C), c0, tid);
+  }
+
+  // outputs of token tile tb of one chunk (lane: token 16tb + lr, columns
+  // c0 + cw + 16j + 4lg .. +3)
+  auto store_tile = [&](int chunk, int tb) __attribute__((always_inline)) {
+    const int nv = min(C, a.T - chunk * C);
+    const size_t base = tok_base(chunk) + c0 + cw + 4 * lg;
+    const bool bf = a.out_bf16 && !a.raw_out;
+#pragma unroll
+    for (int j = 0; j < CBW; ++j) {
+      if (16 * tb + lr < nv) {
+        const size_t idx = base + (size_t)(16 * tb + lr) * tok_stride + 16 * j;
+        const float4 x4 = make_float4(op[tb][j][0], op[tb][j][1], op[tb][j][2], op[tb][j][3]);
+        if (bf) store4<true>(a.o, idx, x4);
+        else store4<false>(a.o, idx, x4);
+      }
+    }
+  };
+  // checkpoint: the state after a chunk that ends on a multiple of ckpt_every tokens
+  auto store_ckpt = [&](int chunk) __attribute__((always_inline)) {
+    const int t0 = chunk * C, nv = min(C, a.T - t0);
+    if (a.ckpt_every > 0 && nv == C && (t0 + C) % a.ckpt_every == 0) {
+      const int m = (t0 + C) / a.ckpt_every - 1;
+      float *dst = a.ckpt + (((size_t)b * a.n_ckpt + m) * a.H + h) * (size_t)D * D;
+#pragma unroll
+      for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+        for (int j = 0; j < CBW; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            dst[(size_t)(16 * ib + 4 * lg + r) * D + c0 + cw + 16 * j + lr] = S[ib][j][r];
+    }
+  };
+
+  // one chunk, reading record buffer BUF (recA or recB) and filling the other
+  auto step = [&](auto bufc, int chunk) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    unsigned char *rc = BUF == 0 ? recA : recB;
+    unsigned char *rn = BUF == 0 ? recB : recA;
+    __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0): this wave's loads landed
+    __syncthreads();                                   // every wave's; V of this chunk visible
+
+    if constexpr (GATE) {
+#pragma unroll
+      for (int tb = 0; tb < NT; ++tb)
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) gc[tb][j] = gn[tb][j];
+    }
+    const int nx = min(chunk + 1, ch_last);            // the last chunk reloads its own
+    if constexpr (GATE) load_gate(gn, nx);
+    const bool prev = MODE == MODE_OUTPUT && chunk > ch_begin;
+    if (prev) store_ckpt(chunk - 1);
+    // The record copy and the previous chunk's output stores are issued in pieces
+    // between the products below, so that the memory pipeline works while the
+    // matrix cores do.
+
+    auto frag = [&](size_t off, int f) __attribute__((always_inline)) {
+      return Op<F32>::load(reinterpret_cast<const T *>(rc + R::frag(off, f, lane)));
+    };
+    // S and V as operands (contraction over key channels / tokens, split order)
+    V8 sf[4][CBW], vf[KB][CBW];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int j = 0; j < CBW; ++j) sf[kb][j] = frag_from<F32>(S[2 * kb][j], S[2 * kb + 1][j]);
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < CBW; ++j) vf[kb][j] = ld_t_split<F32, NC>(sV, 32 * kb, cw + 16 * j, lane);
+
+    // ===== U = T V - W S: lane holds U[16tb + 4lg + r][cw + 16j + lr] =====
+    f32x4 U[NT][CBW];
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb) {
+      V8 wf[4], tf[KB];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) wf[kb] = frag(R::oW, tb * 4 + kb);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) tf[kb] = frag(R::oT, tb * KB + kb);
+#pragma unroll
+      for (int j = 0; j < CBW; ++j) {
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) acc = Op<F32>::mma(acc, wf[kb], sf[kb][j]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[r] = -acc[r];
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc = Op<F32>::mma(acc, tf[kb], vf[kb][j]);
+        U[tb][j] = acc;
+      }
+      copy_rec(rn, nx, tb * NCOPY / NT, (tb + 1) * NCOPY / NT);
+    }
+    // U as an operand (contraction over tokens; tokens past the chunk are zero)
+    V8 uf[KB][CBW];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int j = 0; j < CBW; ++j) uf[kb][j] = frag_from<F32>(U[2 * kb][j], 2 * kb + 1 < NT ? U[2 * kb + 1][j] : zero4());
+
+    // ===== O^T = S^T Qt^T + U^T P^T: lane holds O[16tb + lr][cw + 16j + 4lg + r] =====
+    f32x4 O[NT][CBW];
+    if constexpr (MODE == MODE_OUTPUT) {
+#pragma unroll
+      for (int tb = 0; tb < NT; ++tb) {
+        V8 qf[4], pf[KB];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) qf[kb] = frag(R::oQ, tb * 4 + kb);
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) pf[kb] = frag(R::oP, tb * KB + kb);
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) {
+          f32x4 acc = zero4();
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) acc = Op<F32>::mma(acc, sf[kb][j], qf[kb]);
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) acc = Op<F32>::mma(acc, uf[kb][j], pf[kb]);
+          O[tb][j] = acc;
+        }
+        if (prev) store_tile(chunk - 1, tb);
+      }
+    }
+
+    // ===== S <- Diag(e^{G_C}) S + Kdec^T U =====
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib) {
+      const float4 dec = *reinterpret_cast<const float4 *>(rc + R::oDec + 4 * (16 * ib + 4 * lg));
+      V8 kf[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) kf[kb] = frag(R::oK, ib * KB + kb);
+#pragma unroll
+      for (int j = 0; j < CBW; ++j) {
+        f32x4 acc = S[ib][j];
+        acc[0] *= dec.x; acc[1] *= dec.y; acc[2] *= dec.z; acc[3] *= dec.w;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) acc = Op<F32>::mma(acc, kf[kb], uf[kb][j]);
+        S[ib][j] = acc;
+      }
+    }
+
+    // per-token sums of squares of this wave's columns for the fused RMSNorm
+    if constexpr (GATE) {
+#pragma unroll
+      for (int tb = 0; tb < NT; ++tb) {
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < CBW; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ss += O[tb][j][r] * O[tb][j][r];
+        ss += __shfl_xor(ss, 16, 64);
+        ss += __shfl_xor(ss, 32, 64);
+        if (lg == 0) sNorm[wave * C + 16 * tb + lr] = ss;
+      }
+    }
+    // Norm partials visible and every wave done with this chunk's V.  A barrier without
+    // a memory fence: a fence would wait for the record copy in flight.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0): own LDS accesses done
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    {                                                  // values of chunk+1 (loaded a chunk ago)
+      const int n1 = min(chunk + 1, ch_last);
+      store_v<C, NC, F32, MODE>(sV, vr, min(C, a.T - n1 * C), c0, tid);
+    }
+    {
+      const int n2 = min(chunk + 2, ch_last);
+      load_v<C, NC, F32, MODE>(vr, a, tok_base(n2), min(C, a.T - n2 * C), c0, tid);
+    }
+
+    if constexpr (MODE == MODE_OUTPUT) {
+      if constexpr (GATE) {
+        // per-head RMSNorm over the 128 value columns, then the sigmoid gate
+#pragma unroll
+        for (int tb = 0; tb < NT; ++tb) {
+          const int t = 16 * tb + lr;
+          const float tot = sNorm[t] + sNorm[C + t] + sNorm[2 * C + t] + sNorm[3 * C + t];
+          const float inv = rsqrtf(tot * (1.0f / D) + a.eps);
+#pragma unroll
+          for (int j = 0; j < CBW; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              op[tb][j][r] = O[tb][j][r] * inv * wv[j][r] * sigmoidf_(q4_at<F32>(gc[tb][j], r));
+        }
+      } else {
+#pragma unroll
+        for (int tb = 0; tb < NT; ++tb)
+#pragma unroll
+          for (int j = 0; j < CBW; ++j) op[tb][j] = O[tb][j];
+      }
+    }
+  };
+  for (int chunk = ch_begin; chunk < ch_end; chunk += 2) {
+    step(std::integral_constant<int, 0>{}, chunk);
+    if (chunk + 1 < ch_end) step(std::integral_constant<int, 1>{}, chunk + 1);
+  }
+  if constexpr (MODE == MODE_OUTPUT) {
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb) store_tile(ch_last, tb);
+    store_ckpt(ch_last);
+  }
+
+  // ---- results: the final state (last segment) or the segment map
+  if constexpr (MODE == MODE_OUTPUT) {
+    if (a.S_final && seg == a.n_seg - 1) {
+#pragma unroll
+      for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+        for (int j = 0; j < CBW; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            a.S_final[state_off + (size_t)(16 * ib + 4 * lg + r) * D + c0 + cw + 16 * j + lr] = S[ib][j][r];
+    }
+  } else {
+    float *dst = a.maps + (size_t)unit * D * (2 * D);
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+      for (int j = 0; j < CBW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          dst[(size_t)(16 * ib + 4 * lg + r) * (2 * D) + c0 + cw + 16 * j + lr] = S[ib][j][r];
+  }
+  // the copies of the last iteration (a reload of the last chunk) complete before the
+  // workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// ---------------------------------------------------------------------------
+// associative scan of segment maps: S_in[0] = S0, S_in[s+1] = A_s S_in[s] + B_s
+// ("xhh.club" structure entry: context parallelism by an associative prefix scan; the
+// states entering later segments are composed, never summed).  One workgroup per
+// (sequence, head, 16-column block); the map product runs as fp32 MFMA.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *__restrict__ maps,
+                                                           const float *__restrict__ S0,
+                                                           float *__restrict__ sin, int n_seg,
+                                                           int n_bh) {
+  __shared__ __align__(16) float sXt[16][D + 4];      // current state block, transposed [n][i]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int bh = blockIdx.x / (D / 16), cb = blockIdx.x % (D / 16);
+  if (bh >= n_bh) return;
+  const int c0 = cb * 16;
+  // S_in[0] = S0 (or zeros)
+  for (int x = tid; x < 16 * D; x += NTHREADS) {
+    const int i = x / 16, n = x % 16;
+    const float v = S0 ? S0[(size_t)bh * D * D + (size_t)i * D + c0 + n] : 0.f;
+    sXt[n][i] = v;
+    sin[((size_t)bh * n_seg) * D * D + (size_t)i * D + c0 + n] = v;
+  }
+  __syncthreads();
+  for (int s = 0; s + 1 < n_seg; ++s) {
+    const float *A = maps + ((size_t)bh * n_seg + s) * D * (2 * D);
+    f32x4 acc[2];
+    // wave w computes rows 32w..32w+31 (two 16-row tiles); lane group g supplies
+    // contraction indices 32g .. 32g+31 (one per MFMA).
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int i = (2 * wave + it) * 16 + lr;
+      f32x4 c = zero4();
+      const float *arow = A + (size_t)i * (2 * D) + 32 * lg;
+#pragma unroll
+      for (int q4 = 0; q4 < 8; ++q4) {
+        const float4 av = *reinterpret_cast<const float4 *>(arow + 4 * q4);
+        const float4 bv = *reinterpret_cast<const float4 *>(&sXt[lr][32 * lg + 4 * q4]);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, c, 0, 0, 0);
+      }
+      acc[it] = c;
+    }
+    __syncthreads();   // all reads of the old block done
+    float *dst = sin + ((size_t)bh * n_seg + s + 1) * D * D;
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = (2 * wave + it) * 16 + 4 * lg + r;
+        const float v = acc[it][r] + A[(size_t)i * (2 * D) + D + c0 + lr];
+        sXt[lr][i] = v;
+        dst[(size_t)i * D + c0 + lr] = v;
+      }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm + sigmoid gate over raw outputs (used when the value columns of a head are
+// split across workgroups): one wave per 4 (token, head) rows.
+// ---------------------------------------------------------------------------
+template <bool IN_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(NTHREADS) void norm_gate_kernel(const float *__restrict__ raw,
+                                                             const void *__restrict__ gate,
+                                                             const float *__restrict__ w,
+                                                             void *__restrict__ out, int64_t rows,
+                                                             float eps) {
+  const int lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int64_t row = ((int64_t)blockIdx.x * (NTHREADS / 64) + (threadIdx.x >> 6)) * 4 + lg;
+  if (row >= rows) return;
+  const size_t base = (size_t)row * D + 8 * lr;
+  const float4 a0 = *reinterpret_cast<const float4 *>(raw + base);
+  const float4 a1 = *reinterpret_cast<const float4 *>(raw + base + 4);
+  const float ov[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ss += ov[e] * ov[e];
+  ss += __shfl_xor(ss, 1, 64);
+  ss += __shfl_xor(ss, 2, 64);
+  ss += __shfl_xor(ss, 4, 64);
+  ss += __shfl_xor(ss, 8, 64);
+  const float inv = rsqrtf(ss * (1.0f / D) + eps);
+  const float4 g0 = load4<IN_BF16>(gate, base), g1 = load4<IN_BF16>(gate, base + 4);
+  const float gv[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+  float res[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) res[e] = ov[e] * inv * (w ? w[8 * lr + e] : 1.f) * sigmoidf_(gv[e]);
+  store4<OUT_BF16>(out, base, make_float4(res[0], res[1], res[2], res[3]));
+  store4<OUT_BF16>(out, base + 4, make_float4(res[4], res[5], res[6], res[7]));
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+template <int C, int NC, bool F32, int MODE, bool GATE>
+hipError_t launch_one(const StateArgs &a, hipStream_t s) {
+  constexpr int VS = (MODE == MODE_TRANSITION ? 2 * D : D) / NC;
+  const int groups = (a.n_units + 7) / 8;
+  const unsigned grid = static_cast<unsigned>(groups) * 8u * VS;
+  hipLaunchKernelGGL((chunk_state_kernel<C, NC, F32, MODE, GATE>), dim3(grid), dim3(NTHREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int C, bool F32, int MODE>
+hipError_t launch_nc(const StateArgs &a, int nc, hipStream_t s) {
+  if (nc == 128) {
+    if constexpr (MODE == MODE_OUTPUT) {
+      if (a.fused_gate) return launch_one<C, 128, F32, MODE, true>(a, s);
+    }
+    return launch_one<C, 128, F32, MODE, false>(a, s);
+  }
+  if (nc == 64) return launch_one<C, 64, F32, MODE, false>(a, s);
+  return hipErrorInvalidValue;
+}
+
+template <int MODE>
+hipError_t launch_mode(const StateArgs &a, int chunk, bool f32, int nc, hipStream_t s) {
+  if (f32) return launch_nc<16, true, MODE>(a, nc, s);
+  if (chunk == 16) return launch_nc<16, false, MODE>(a, nc, s);
+  return launch_nc<64, false, MODE>(a, nc, s);
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const kda_prefill_desc &d, const PrefillPlan &p, hipStream_t s) {
+  const bool f32 = d.in_dtype == KDA_F32;
+  const int64_t units = (int64_t)d.B * d.H;
+
+  if (d.T == 0) {
+    // no tokens: the final state is the initial state
+    if (d.S_final && d.S_final != d.S0) {
+      if (d.S0) return launch_state_copy(d.S_final, d.S0, units * d.d_k * d.d_v, s);
+      return launch_fill_zero(d.S_final, units * d.d_k * d.d_v, s);
+    }
+    return hipSuccess;
+  }
+
+  unsigned char *ws = static_cast<unsigned char *>(d.workspace);
+  unsigned char *rec = ws + p.off_rec;
+  float *maps = p.ws_maps ? reinterpret_cast<float *>(ws + p.off_maps) : nullptr;
+  float *sin = p.ws_sin ? reinterpret_cast<float *>(ws + p.off_sin) : nullptr;
+
+  // pass 0: per-chunk records, all chunks in parallel
+  hipError_t e = launch_prefill_prep(d, p.n_chunks, rec, s);
+  if (e != hipSuccess) return e;
+
+  StateArgs a{};
+  a.v = d.v; a.gate = d.gate;
+  a.S0 = d.S0; a.norm_weight = d.norm_weight;
+  a.rec = rec;
+  a.S_final = d.S_final; a.ckpt = d.ckpt; a.o = d.o;
+  a.maps = maps; a.sin = sin; a.eps = d.norm_eps;
+  a.T = d.T; a.H = d.H;
+  a.n_seg = p.n_seg; a.seg_chunks = p.seg_chunks; a.n_chunks = p.n_chunks;
+  a.ckpt_every = d.ckpt_every;
+  a.n_ckpt = d.ckpt_every > 0 ? d.T / d.ckpt_every : 0;
+  a.out_bf16 = d.out_dtype == KDA_BF16;
+  a.n_units = static_cast<int>(units * p.n_seg);
+  const int nc = D / p.v_split;
+  a.fused_gate = d.gate != nullptr && !p.split_norm;
+  a.raw_out = p.split_norm;
+  float *raw = nullptr;
+  if (p.split_norm) {
+    // raw o goes to fp32 storage first: the output itself when it is fp32
+    raw = d.out_dtype == KDA_F32 ? static_cast<float *>(d.o) : reinterpret_cast<float *>(ws + p.off_norm);
+    a.o = raw;
+  }
+
+  if (p.n_seg > 1) {
+    // pass 1: maps of all segments but the last
+    StateArgs t = a;
+    t.fused_gate = 0;
+    // the map [A | B] has 2 x 128 columns: two workgroups per segment
+    e = launch_mode<MODE_TRANSITION>(t, d.chunk, f32, D, s);
+    if (e != hipSuccess) return e;
+    // pass 2: states entering each segment
+    const unsigned grid = static_cast<unsigned>(units * (D / 16));
+    hipLaunchKernelGGL(segment_scan, dim3(grid), dim3(NTHREADS), 0, s, maps, d.S0, sin, p.n_seg,
+                       static_cast<int>(units));
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // pass 3 (or the single pass): outputs, checkpoints, final state
+  e = launch_mode<MODE_OUTPUT>(a, d.chunk, f32, nc, s);
+  if (e != hipSuccess) return e;
+  if (p.split_norm) {
+    const int64_t rows = (int64_t)d.B * d.T * d.H;
+    const unsigned grid = static_cast<unsigned>((rows + 15) / 16);
+    const bool ib = d.in_dtype == KDA_BF16, ob = d.out_dtype == KDA_BF16;
+    if (ib && ob) hipLaunchKernelGGL((norm_gate_kernel<true, true>), dim3(grid), dim3(NTHREADS), 0, s, raw, d.gate, d.norm_weight, d.o, rows, d.norm_eps);
+    else if (ib) hipLaunchKernelGGL((norm_gate_kernel<true, false>), dim3(grid), dim3(NTHREADS), 0, s, raw, d.gate, d.norm_weight, d.o, rows, d.norm_eps);
+    else if (ob) hipLaunchKernelGGL((norm_gate_kernel<false, true>), dim3(grid), dim3(NTHREADS), 0, s, raw, d.gate, d.norm_weight, d.o, rows, d.norm_eps);
+    else hipLaunchKernelGGL((norm_gate_kernel<false, false>), dim3(grid), dim3(NTHREADS), 0, s, raw, d.gate, d.norm_weight, d.o, rows, d.norm_eps);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace kda

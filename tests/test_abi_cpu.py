@@ -58,6 +58,10 @@ def _desc(**over):
     d.v_split, d.n_segments = 1, 1
     for k, v in over.items():
         setattr(d, k, v)
+    # every prefill with tokens needs a workspace for its per-chunk records
+    n = C.c_size_t(0)
+    if _lib.load().kda_prefill_workspace_size(C.byref(d), C.byref(n)) == kda.KDA_OK:
+        d.workspace, d.workspace_bytes = FAKE + (1 << 36), n.value
     return d
 
 
@@ -80,6 +84,7 @@ def test_prefill_validation_errors():
     assert _call(_desc(chunk=32)) == kda.KDA_ERR_UNSUPPORTED
     assert _call(_desc(in_dtype=7)) == kda.KDA_ERR_UNSUPPORTED
     assert _call(_desc(v_split=3)) == kda.KDA_ERR_UNSUPPORTED
+    assert _call(_desc(v_split=4)) == kda.KDA_ERR_UNSUPPORTED
     assert _call(_desc(B=-1)) == kda.KDA_ERR_SHAPE
     assert _call(_desc(ckpt_every=100)) == kda.KDA_ERR_SHAPE
     assert _call(_desc(n_segments=3)) == kda.KDA_ERR_SHAPE           # 2 chunks only
@@ -88,11 +93,13 @@ def test_prefill_validation_errors():
     d = _desc()
     d.o = d.k + 100                                                  # o overlaps k
     assert _call(d) == kda.KDA_ERR_ALIAS
-    d = _desc(n_segments=2)                                          # needs a workspace
+    d = _desc(n_segments=2)
+    d.workspace, d.workspace_bytes = None, 0                         # needs a workspace
     assert _call(d) == kda.KDA_ERR_WORKSPACE
     n = C.c_size_t(0)
     assert lib.kda_prefill_workspace_size(C.byref(d), C.byref(n)) == kda.KDA_OK
-    assert n.value >= 2 * 4 * 2 * 3 * 128 * 128 * 4
+    # per-chunk records (2 chunks x 8 heads) + maps and entering states of 2 segments
+    assert n.value >= 2 * 4 * 2 * 66048 + 2 * 4 * 2 * 3 * 128 * 128 * 4
     d.workspace, d.workspace_bytes = FAKE + (1 << 36), n.value - 1
     assert _call(d) == kda.KDA_ERR_WORKSPACE
     assert lib.kda_prefill_workspace_size(C.byref(_desc()), None) == kda.KDA_ERR_NULL
@@ -106,6 +113,7 @@ def test_empty_prefill_is_a_noop():
 @pytest.mark.skipif(_gpu_present(), reason="checks the no-device error path")
 def test_prefill_without_device_reports_device_error():
     assert _call(_desc()) == kda.KDA_ERR_DEVICE
+    assert _call(_desc(v_split=2)) == kda.KDA_ERR_DEVICE     # both column splits validate
 
 
 def _ddesc(**over):

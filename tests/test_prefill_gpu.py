@@ -84,7 +84,7 @@ def test_bf16_small_ragged(T, chunk):
     check(c, f"bf16 T={T} chunk={chunk}", chunk=chunk, v_split=1)
 
 
-@pytest.mark.parametrize("v_split", [1, 2, 4])
+@pytest.mark.parametrize("v_split", [1, 2])
 def test_bf16_v_split(v_split):
     c = make_prefill(1, 300, 3, 128, seed=11, in_dtype=BF16, s0_std=0.05)
     check(c, f"bf16 v_split={v_split}", chunk=64, v_split=v_split)
@@ -97,9 +97,10 @@ def test_f32_tiny_workload(seed):
     check(c, f"f32 tiny seed={seed}", TOL_O_F32, TOL_S_F32, chunk=16, S0=False)
 
 
-def test_f32_ragged_with_state():
+@pytest.mark.parametrize("v_split", [1, 2])
+def test_f32_ragged_with_state(v_split):
     c = make_prefill(2, 37, 3, 128, seed=5, in_dtype=F32, s0_std=0.1)
-    check(c, "f32 ragged", TOL_O_F32, TOL_S_F32, chunk=16, v_split=4)
+    check(c, f"f32 ragged v_split={v_split}", TOL_O_F32, TOL_S_F32, chunk=16, v_split=v_split)
 
 
 def test_bf16_on_tiny_shapes():
@@ -138,7 +139,7 @@ def test_beta_one():
 # ---------------------------------------------------------------------------
 # norm + gate, checkpoints, segments
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("v_split", [1, 4])
+@pytest.mark.parametrize("v_split", [1, 2])
 def test_norm_gate(v_split):
     c = make_prefill(2, 320, 2, 128, seed=31, in_dtype=BF16, s0_std=0.01, gate=True)
     w = np.random.default_rng(31).uniform(0.5, 1.5, 128).astype(np.float32)
@@ -174,8 +175,8 @@ def test_segment_count_agreement():
 
 def test_deterministic():
     c = make_prefill(2, 200, 2, 128, seed=61, in_dtype=BF16, s0_std=0.05, gate=True)
-    o1, S1, _ = run_gpu(c, gate=True, v_split=2)
-    o2, S2, _ = run_gpu(c, gate=True, v_split=2)
+    o1, S1, _ = run_gpu(c, gate=True, v_split=1)
+    o2, S2, _ = run_gpu(c, gate=True, v_split=1)
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 

@@ -30,21 +30,24 @@ def _say(*a):
     print(*a, flush=True, file=sys.stderr)
 
 
-@pytest.mark.parametrize("v_split", [0, 1])
-def test_prefill_8k_all_heads(v_split):
-    _say(f"prefill_8k v_split={v_split}: generating")
+@pytest.mark.parametrize("v_split,n_seg", [(0, 0), (1, 1), (2, 1)])
+def test_prefill_8k_all_heads(v_split, n_seg):
+    """(0, 0) is the automatic plan the benchmark times; (1, 1) one pass over whole
+    heads; (2, 1) split columns with the separate norm pass."""
+    _say(f"prefill_8k v_split={v_split} n_seg={n_seg}: generating")
     c = make_workload("prefill_8k", seed=0)
     o = torch.empty((c.B, c.T, c.H, 128), dtype=torch.float32, device=dev())
     S = torch.empty((c.B, c.H, 128, 128), dtype=torch.float32, device=dev())
     kda.kda_prefill_chunked(up(c.q), up(c.k), up(c.v), up(c.g), up(c.beta), o=o, S0=up(c.S0),
-                            S_final=S, gate=up(c.gate), norm_eps=1e-6, chunk=64, v_split=v_split)
+                            S_final=S, gate=up(c.gate), norm_eps=1e-6, chunk=64, v_split=v_split,
+                            n_segments=n_seg)
     torch.cuda.synchronize()
     _say("prefill_8k: oracle")
     o_ref, S_ref, _ = native.prefill(c.q, c.k, c.v, c.g, c.beta, c.S0, bf16=True)
     o_ref = norm_gate(o_ref, to_f64(c.gate, BF16), 1e-6)
     og = down(o)
     eo, es = err_o(og, o_ref), err_S(down(S), S_ref)
-    _say(f"prefill_8k v_split={v_split}: err_o={eo:.3e} err_S={es:.3e}")
+    _say(f"prefill_8k v_split={v_split} n_seg={n_seg}: err_o={eo:.3e} err_S={es:.3e}")
     assert np.isfinite(og).all()
     assert eo <= TOL_O and es <= TOL_S
 
