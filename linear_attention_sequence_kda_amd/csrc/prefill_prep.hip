@@ -47,27 +47,29 @@ struct PrepLayout {
   static constexpr int KC = C < 32 ? 32 : C;          // token contraction extent (zero padded)
   static constexpr size_t E = sizeof(T);
   static constexpr size_t al(size_t x) { return (x + 15) & ~size_t(15); }
-  static constexpr int AOL = C + 8;                   // padded row of the off-diagonal A (fp16)
+  static constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
   static constexpr int NFAC = NT > 2 ? (NT - 1) * (NT - 2) / 2 : 1;   // tile pairs w - s' >= 2
+  static constexpr int NBO = NT * (NT - 1) / 2;       // off-diagonal blocks of A below the diagonal
   static constexpr size_t bKT = (size_t)KC * D * E;   // K e^G      [t][i]  (rows >= C zero)
-  static constexpr size_t bKF = (size_t)KC * D * E;   // KF [t][i] (rows >= C zero), then W [t][i]
-  static constexpr size_t bPt = (size_t)KC * C * E;   // P^T        [j][t]  (rows >= C zero)
+  static constexpr size_t bKF = (size_t)KC * D * E;   // KF         [t][i]  (rows >= C zero)
   static constexpr size_t bTt = (size_t)KC * C * E;   // T^T        [j][t]  (rows >= C zero)
   static constexpr size_t bAd = (size_t)NT * 256 * 4; // diagonal blocks of A, fp32
-  static constexpr size_t bAo = NT > 1 ? (size_t)C * AOL * 2 : 0;   // A, off-diagonal blocks
-  static constexpr size_t bX = (size_t)NT * 256 * 4;  // inverses of the diagonal blocks of I + A
+  static constexpr size_t bVec = (size_t)(3 * NT + NFAC) * D * 4;   // per-tile decay vectors
+  static constexpr size_t bAo = NBO > 0 ? (size_t)NBO * 256 * 2 : 0;   // A, off-diagonal blocks, fp16
+  static constexpr size_t bX = (size_t)NT * 256 * E;  // inverses of the diagonal blocks of I + A
   static constexpr size_t oKT = 0;
   static constexpr size_t oKF = al(oKT + bKT);
-  static constexpr size_t oPt = al(oKF + bKF);
-  static constexpr size_t oTt = al(oPt + bPt);
-  static constexpr size_t oAd = al(oTt + bTt);
-  static constexpr size_t oAo = al(oAd + bAd);
-  static constexpr size_t oX = al(oAo + bAo);
-  static constexpr size_t oDpow = al(oX + bX);                  // D_m = e^{tile m total}
+  // T^T is written only after the diagonal A blocks and the per-tile vectors are dead,
+  // so it shares their storage
+  static constexpr size_t oTt = al(oKF + bKF);
+  static constexpr size_t oAd = oTt;
+  static constexpr size_t oDpow = oAd + bAd;                    // D_m = e^{tile m total}
   static constexpr size_t oPre = oDpow + (size_t)NT * D * 4;    // prod_{m<w} D_m
   static constexpr size_t oPost = oPre + (size_t)NT * D * 4;    // prod_{m>w} D_m
   static constexpr size_t oFac = oPost + (size_t)NT * D * 4;    // prod_{s'<m<w} D_m
-  static constexpr size_t oBeta = oFac + (size_t)NFAC * D * 4;
+  static constexpr size_t oAo = al(oTt + cmax(bTt, bAd + bVec));
+  static constexpr size_t oX = al(oAo + bAo);
+  static constexpr size_t oBeta = al(oX + bX);
   static constexpr size_t oDecay = oBeta + (size_t)KC * 4;
   static constexpr size_t bytes = al(oDecay + D * 4);
 };
@@ -155,12 +157,10 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
   extern __shared__ __align__(16) unsigned char smem[];
   T *sKT = reinterpret_cast<T *>(smem + L::oKT);       // rows of D
   T *sKF = reinterpret_cast<T *>(smem + L::oKF);       // rows of D
-  T *sW = sKF;                                         // W [t][i], after KF is dead
-  T *sPt = reinterpret_cast<T *>(smem + L::oPt);       // rows of C
   T *sTt = reinterpret_cast<T *>(smem + L::oTt);       // rows of C
   float *sAd = reinterpret_cast<float *>(smem + L::oAd);
   _Float16 *sAo = reinterpret_cast<_Float16 *>(smem + L::oAo);
-  float *sX = reinterpret_cast<float *>(smem + L::oX);
+  T *sX = reinterpret_cast<T *>(smem + L::oX);
   float *sDpow = reinterpret_cast<float *>(smem + L::oDpow);
   float *sPre = reinterpret_cast<float *>(smem + L::oPre);
   float *sPost = reinterpret_cast<float *>(smem + L::oPost);
@@ -172,10 +172,10 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
   const int lr = lane & 15, lg = lane >> 4;
   const int tt = 16 * wave + lr;                       // this lane's token in phase A
 
-  // zero the padded token range of the contraction buffers once (only when KC > C)
+  // zero the padded token range of the contraction buffers (only when KC > C; the
+  // rows of T^T past the chunk are cleared in the solve, when its storage is free)
   if constexpr (KC > C) {
     for (int x = tid; x < (KC - C) * D; x += NTHREADS) { sKT[C * D + x] = T(0); sKF[C * D + x] = T(0); }
-    for (int x = tid; x < (KC - C) * C; x += NTHREADS) { sPt[C * C + x] = T(0); sTt[C * C + x] = T(0); }
   }
 
   const int64_t rec = blockIdx.x;
@@ -247,8 +247,14 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
 
     // ===== A2: decay factors, diagonal tile, chunk-level operands =====
     V8 rkx[4], rqx[4];                                 // k e^{G_t - r_w}, q e^{G_t - r_w}
+    // P is formed transposed: a P^T tile (s, w) in MFMA output layout holds, per lane,
+    // token 16w + lr and keys 16s + 4lg + r, which are exactly the lane's elements of
+    // P's split-order operand fragment, so P is exported without going through LDS
+    f32x4 accPd = zero4(), accP[NT];                   // P^T tiles (w, w) and (s', w)
+#pragma unroll
+    for (int sp = 0; sp < NT; ++sp) accP[sp] = zero4();
     if (wave < NT) {
-      f32x4 accAd = zero4(), accPd = zero4();          // diagonal tile (w, w)
+      f32x4 accAd = zero4();                           // diagonal tile (w, w) of A
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const int ch = 32 * kb + 4 * lg;               // channels ch + (0..3), ch + 16 + (0..3)
@@ -285,7 +291,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
           const V8 vq{rq[0], rq[1], rq[2], rq[3], rq[4], rq[5], rq[6], rq[7]};
           const V8 vy{yd[0], yd[1], yd[2], yd[3], yd[4], yd[5], yd[6], yd[7]};
           accAd = Op<true>::mma(accAd, va, vy);
-          accPd = Op<true>::mma(accPd, vq, vy);
+          accPd = Op<true>::mma(accPd, vy, vq);
         } else {
           bf16x8 kh, yh, qh, ql, yl;
 #pragma unroll
@@ -297,24 +303,18 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
             yl[e] = static_cast<__bf16>(yd[e] - static_cast<float>(yh[e]));
           }
           accAd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kh, yh, accAd, 0, 0, 0);
-          accPd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, yh, accPd, 0, 0, 0);
-          accPd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh, yl, accPd, 0, 0, 0);
-          accPd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql, yh, accPd, 0, 0, 0);
+          accPd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yh, qh, accPd, 0, 0, 0);
+          accPd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yl, qh, accPd, 0, 0, 0);
+          accPd = __builtin_amdgcn_mfma_f32_16x16x32_bf16(yh, ql, accPd, 0, 0, 0);
         }
       }
-      // diagonal tile: A (beta rows, strictly lower, fp32), P^T (lower incl.), and
-      // P's zero blocks above the diagonal of this tile row
-      float pv[4];
+      // diagonal tile: A (beta rows, strictly lower, fp32); P^T keeps keys j <= t
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int ti = 4 * lg + r, t = 16 * wave + ti;
         sAd[wave * 256 + ti * 16 + lr] = ti > lr ? accAd[r] * sBeta[t] : 0.f;
-        pv[r] = ti >= lr ? accPd[r] : 0.f;
+        accPd[r] = ti <= lr ? accPd[r] : 0.f;
       }
-      st4<F32, C>(sPt, 16 * wave + lr, 16 * wave + 4 * lg, pv[0], pv[1], pv[2], pv[3]);
-#pragma unroll
-      for (int sp = 1; sp < NT; ++sp)
-        if (sp > wave) st4<F32, C>(sPt, 16 * sp + lr, 16 * wave + 4 * lg, 0.f, 0.f, 0.f, 0.f);
     }
     __syncthreads();   // KF, Kt, decay, diagonal A/P visible
 
@@ -337,12 +337,12 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
       invert_unit_lower(rowA, x, j, std::make_integer_sequence<int, 16>{});
       if (bb < NT) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sX[bb * 256 + i * 16 + j] = x[i];
+        for (int i = 0; i < 16; ++i) sX[bb * 256 + i * 16 + j] = static_cast<T>(x[i]);
       }
     } else if (wave < NT) {
-      f32x4 accA[NT], accP[NT];
+      f32x4 accA[NT];
 #pragma unroll
-      for (int sp = 0; sp < NT; ++sp) { accA[sp] = zero4(); accP[sp] = zero4(); }
+      for (int sp = 0; sp < NT; ++sp) accA[sp] = zero4();
 #pragma unroll
       for (int sp = 0; sp < NT - 1; ++sp) {
         if (sp < wave) {
@@ -363,7 +363,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
             }
             const V8 vb = ld_n_split<F32, D>(sKF, 16 * sp, 32 * kb, lane);
             accA[sp] = Op<F32>::mma(accA[sp], va, vb);
-            accP[sp] = Op<F32>::mma(accP[sp], vq, vb);
+            accP[sp] = Op<F32>::mma(accP[sp], vb, vq);
           }
         }
       }
@@ -371,14 +371,25 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
       for (int sp = 0; sp < NT - 1; ++sp) {
         if (sp < wave) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
+          for (int r = 0; r < 4; ++r) {               // block (w, s'), row 4lg + r, column lr
             const int t = 16 * wave + 4 * lg + r;
-            sAo[t * L::AOL + 16 * sp + lr] = static_cast<_Float16>(accA[sp][r] * sBeta[t]);
+            sAo[((wave * (wave - 1)) / 2 + sp) * 256 + (4 * lg + r) * 16 + lr] =
+                static_cast<_Float16>(accA[sp][r] * sBeta[t]);
           }
-          st4<F32, C>(sPt, 16 * sp + lr, 16 * wave + 4 * lg, accP[sp][0], accP[sp][1], accP[sp][2], accP[sp][3]);
         }
       }
     }
+    // P fragments (tile w, kb) from the P^T tiles (2kb, w) and (2kb + 1, w)
+    if (wave < NT) {
+      auto pt = [&](int sp) __attribute__((always_inline)) {
+        return sp < wave ? accP[sp] : sp == wave ? accPd : zero4();
+      };
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        Op<F32>::store(reinterpret_cast<T *>(out + R::frag(R::oP, wave * KB + kb, lane)),
+                       frag_from<F32>(pt(2 * kb), pt(2 * kb + 1)));
+    }
+
     // Kdec^T fragments: Kdec = KF * prod_{m>w} D_m, read transposed from KF.  Lane
     // (lr, lg) of fragment (ib, kb) holds channel 16ib + lr of tokens 32kb + 4lg + e
     // (tile 2kb) and 32kb + 16 + 4lg + e (tile 2kb + 1).
@@ -397,6 +408,9 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
     // X_{s,w} = -X_ss sum_{w<=m<s} A_{s,m} X_{m,w}; a 16x16 result in MFMA output layout
     // is the B operand layout of the K=16 MFMA, so the blocks stay in registers.
     // Then T[:, block w] = X[:, block w] diag(beta), stored as T^T [j][t]. =====
+    if constexpr (KC > C) {                           // T^T rows past the chunk
+      for (int x = tid; x < (KC - C) * C; x += NTHREADS) sTt[C * C + x] = T(0);
+    }
     if (wave < NT) {
       const int n = lr;                                 // column within the block
       const float bj = sBeta[16 * wave + n];
@@ -405,7 +419,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
       for (int s = 0; s < NT; ++s) {
         if (s == wave) {
 #pragma unroll
-          for (int r = 0; r < 4; ++r) xc[s][r] = sX[wave * 256 + (4 * lg + r) * 16 + n];
+          for (int r = 0; r < 4; ++r) xc[s][r] = static_cast<float>(sX[wave * 256 + (4 * lg + r) * 16 + n]);
         } else {
           xc[s] = zero4();
         }
@@ -418,13 +432,12 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
 #pragma unroll
             for (int m = 0; m < NT - 1; ++m) {
               if (m >= wave && m < s) {
-                const f16x4 a4 = *reinterpret_cast<const f16x4 *>(sAo + (16 * s + lr) * L::AOL + 16 * m + 4 * lg);
+                const f16x4 a4 = *reinterpret_cast<const f16x4 *>(sAo + ((s * (s - 1)) / 2 + m) * 256 + lr * 16 + 4 * lg);
                 const f16x4 b4{(_Float16)xc[m][0], (_Float16)xc[m][1], (_Float16)xc[m][2], (_Float16)xc[m][3]};
                 y = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, b4, y, 0, 0, 0);
               }
             }
-            const float4 xv = *reinterpret_cast<const float4 *>(sX + s * 256 + lr * 16 + 4 * lg);
-            const f16x4 a4{(_Float16)xv.x, (_Float16)xv.y, (_Float16)xv.z, (_Float16)xv.w};
+            const f16x4 a4 = *reinterpret_cast<const f16x4 *>(reinterpret_cast<const _Float16 *>(sX) + s * 256 + lr * 16 + 4 * lg);
             const f16x4 b4{(_Float16)y[0], (_Float16)y[1], (_Float16)y[2], (_Float16)y[3]};
             const f32x4 z = __builtin_amdgcn_mfma_f32_16x16x16f16(a4, b4, zero4(), 0, 0, 0);
 #pragma unroll
@@ -441,45 +454,24 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
     }
     __syncthreads();   // T complete
 
-    // ===== W^T = Kt^T T^T  ->  W [t][i] (over KF) =====
-    {
-      constexpr int NTILE = 8 * NT;                    // (i-block, t-block)
-#pragma unroll 2
-      for (int it = 0; it < (NTILE + 3) / 4; ++it) {
-        const int tile = wave + 4 * it;
-        if (tile < NTILE) {
-          const int ib = tile / NT, tb = tile % NT;
-          f32x4 acc = zero4();
+    // ===== W = T (K e^G): fragment (tb, kb) straight from the two W^T tiles (2kb, tb)
+    // and (2kb + 1, tb), each W^T = Kt^T T^T over the chunk's tokens =====
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-            acc = Op<F32>::mma(acc, ld_t<F32, D>(sKT, 32 * kb, 16 * ib, lane),
-                               ld_t<F32, C>(sTt, 32 * kb, 16 * tb, lane));
-          // acc[r] = W^T[16ib + 4lg + r][16tb + lr]
-          st4<F32, D>(sW, 16 * tb + lr, 16 * ib + 4 * lg, acc[0], acc[1], acc[2], acc[3]);
-        }
+    for (int m = 0; m < R::nW / 4; ++m) {
+      const int f = wave + 4 * m, tb = f / 4, kb = f % 4;
+      f32x4 w0 = zero4(), w1 = zero4();
+#pragma unroll
+      for (int kc = 0; kc < KB; ++kc) {
+        const V8 b = ld_t<F32, C>(sTt, 32 * kc, 16 * tb, lane);
+        w0 = Op<F32>::mma(w0, ld_t<F32, D>(sKT, 32 * kc, 32 * kb, lane), b);
+        w1 = Op<F32>::mma(w1, ld_t<F32, D>(sKT, 32 * kc, 32 * kb + 16, lane), b);
       }
+      Op<F32>::store(reinterpret_cast<T *>(out + R::frag(R::oW, f, lane)), frag_from<F32>(w0, w1));
     }
-    __syncthreads();   // W complete
-
-    // ===== export W, P, T fragments and the chunk decay =====
-    constexpr int NEXP = R::nW + R::nP + R::nT;
-    for (int f = wave; f < NEXP; f += 4) {
-      V8 v;
-      size_t off;
-      if (f < R::nW) {
-        v = ld_n_split<F32, D>(sW, 16 * (f / 4), 32 * (f % 4), lane);
-        off = R::frag(R::oW, f, lane);
-      } else if (f < R::nW + R::nP) {
-        const int g = f - R::nW;
-        v = ld_t_split<F32, C>(sPt, 32 * (g % KB), 16 * (g / KB), lane);
-        off = R::frag(R::oP, g, lane);
-      } else {
-        const int g = f - R::nW - R::nP;
-        v = ld_t_split<F32, C>(sTt, 32 * (g % KB), 16 * (g / KB), lane);
-        off = R::frag(R::oT, g, lane);
-      }
-      Op<F32>::store(reinterpret_cast<T *>(out + off), v);
-    }
+    // T fragments and the chunk decay
+    for (int f = wave; f < R::nT; f += 4)
+      Op<F32>::store(reinterpret_cast<T *>(out + R::frag(R::oT, f, lane)),
+                     ld_t_split<F32, C>(sTt, 32 * (f % KB), 16 * (f / KB), lane));
     if (tid < D / 4)
       reinterpret_cast<float4 *>(out + R::oDec)[tid] = reinterpret_cast<const float4 *>(sDecay)[tid];
   }
@@ -488,7 +480,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
 template <int C, bool F32>
 hipError_t launch_prep_t(const PrepArgs &a, hipStream_t s) {
   using L = PrepLayout<C, F32>;
-  static_assert(L::bytes <= 80 * 1024, "two workgroups per CU must fit in LDS");
+  static_assert(L::bytes <= 53 * 1024, "three workgroups per CU must fit in LDS");
   auto kern = chunk_prep_kernel<C, F32>;
   static std::atomic<bool> attr_set{false};   // the attribute is per function, set once
   if (!attr_set.load(std::memory_order_acquire)) {

@@ -50,8 +50,9 @@ struct StateArgs {
 // value columns of one chunk for this workgroup's slice: groups of 8 columns, token-major
 template <int C, int NC, bool F32>
 struct VRaw {
+  static constexpr int NTH = NC * 4;                   // threads of the workgroup (NC / 16 waves)
   static constexpr int NVG = C * NC / 8;
-  static constexpr int NVPT = (NVG + NTHREADS - 1) / NTHREADS;
+  static constexpr int NVPT = (NVG + NTH - 1) / NTH;
   Q8<F32> v[NVPT];
 };
 
@@ -80,7 +81,7 @@ __device__ __forceinline__ void load_v(VRaw<C, NC, F32> &r, const StateArgs &a, 
   const int cv = MODE == MODE_OUTPUT ? c0 : max(c0 - D, 0);
 #pragma unroll
   for (int u = 0; u < VR::NVPT; ++u) {
-    const int x = tid + u * NTHREADS;
+    const int x = tid + u * VR::NTH;
     const int tc = min(x / per_tok, nval - 1);
     r.v[u] = load_q8<F32>(a.v, tok0 + (size_t)tc * tok_stride + cv + (x % per_tok) * 8);
   }
@@ -95,8 +96,8 @@ __device__ __forceinline__ void store_v(typename Op<F32>::T *sV, const VRaw<C, N
   const bool has_v = MODE == MODE_OUTPUT || c0 >= D;
 #pragma unroll
   for (int u = 0; u < VR::NVPT; ++u) {
-    const int x = tid + u * NTHREADS;
-    if (VR::NVG % NTHREADS == 0 || x < VR::NVG) {
+    const int x = tid + u * VR::NTH;
+    if (VR::NVG % VR::NTH == 0 || x < VR::NVG) {
       const Q8<F32> q = keep_if<F32>(r.v[u], has_v && x / per_tok < nval);
       float vv[8];
 #pragma unroll
@@ -128,15 +129,16 @@ __device__ __forceinline__ float q4_at(const Q4<F32> &x, int e) {
 
 // GATE: the output pass of a whole head (NC = 128) with the fused RMSNorm and gate
 template <int C, int NC, bool F32, int MODE, bool GATE>
-__global__ __launch_bounds__(NTHREADS, 1) void chunk_state_kernel(StateArgs a) {
+__global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
   using R = Rec<C, F32>;
   using T = typename Op<F32>::T;
   using V8 = typename Op<F32>::V8;
   constexpr int KC = C < 32 ? 32 : C;
   constexpr int KB = R::KB, NT = C / 16;
-  constexpr int NCW = NC / 4;                          // state columns per wave
+  constexpr int NW = NC / 16;                          // waves: one 16-column block each,
+  constexpr int NTH = NW * 64;                         // two waves per SIMD for NC = 128
+  constexpr int NCW = 16;                              // state columns per wave
   constexpr int CBW = NCW / 16;                        // 16-column blocks per wave
-  static_assert(CBW >= 1, "each wave owns at least one 16-column block");
   static_assert(!GATE || (MODE == MODE_OUTPUT && NC == D), "the fused epilogue needs whole heads");
   constexpr int VS = (MODE == MODE_TRANSITION ? 2 * D : D) / NC;   // workgroups per unit
   constexpr int NBLK = (int)(R::bytes / 1024);         // record size in KiB
@@ -146,7 +148,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void chunk_state_kernel(StateArgs a) {
   __shared__ __align__(16) unsigned char recA[R::bytes];
   __shared__ __align__(16) unsigned char recB[R::bytes];
   __shared__ __align__(16) T sV[KC * NC];              // V [t][c] (rows >= C zero)
-  __shared__ float sNorm[GATE ? 4 * C : 1];            // per-wave sums of squares
+  __shared__ float sNorm[GATE ? NW * C : 1];           // per-wave sums of squares
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -174,7 +176,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void chunk_state_kernel(StateArgs a) {
 
   // V rows past the chunk stay zero (only when KC > C)
   if constexpr (KC > C) {
-    for (int x = tid; x < (KC - C) * NC; x += NTHREADS) sV[C * NC + x] = T(0);
+    for (int x = tid; x < (KC - C) * NC; x += NTH) sV[C * NC + x] = T(0);
   }
 
   // ---- initial state: S[ib][j] holds rows 16ib + 4lg + r, column c0 + cw + 16j + lr
@@ -203,12 +205,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void chunk_state_kernel(StateArgs a) {
   // instruction, lane l's 16 bytes landing at offset 16 l of that KiB (every wave
   // issues the same number of copies, the last KiB possibly twice, so the count of
   // memory operations in flight is known at compile time)
-  constexpr int NCOPY = (NBLK + 3) / 4;                // copies per wave and chunk
+  constexpr int NCOPY = (NBLK + NW - 1) / NW;          // copies per wave and chunk
   auto copy_rec = [&](unsigned char *dst, int chunk, int n0, int n1) __attribute__((always_inline)) {
     const unsigned char *src = rec_bh + (size_t)chunk * R::bytes + 16 * lane;
 #pragma unroll
     for (int n = n0; n < n1; ++n) {
-      const int blk = min(wave + 4 * n, NBLK - 1);
+      const int blk = min(wave + NW * n, NBLK - 1);
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + (size_t)blk * 1024),
                                        (__attribute__((address_space(3))) void *)(dst + (size_t)blk * 1024), 16, 0, 0);
     }
@@ -428,7 +430,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void chunk_state_kernel(StateArgs a) {
 #pragma unroll
         for (int tb = 0; tb < NT; ++tb) {
           const int t = 16 * tb + lr;
-          const float tot = sNorm[t] + sNorm[C + t] + sNorm[2 * C + t] + sNorm[3 * C + t];
+          float tot = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) tot += sNorm[w * C + t];
           const float inv = rsqrtf(tot * (1.0f / D) + a.eps);
 #pragma unroll
           for (int j = 0; j < CBW; ++j)
@@ -582,7 +586,7 @@ hipError_t launch_one(const StateArgs &a, hipStream_t s) {
   constexpr int VS = (MODE == MODE_TRANSITION ? 2 * D : D) / NC;
   const int groups = (a.n_units + 7) / 8;
   const unsigned grid = static_cast<unsigned>(groups) * 8u * VS;
-  hipLaunchKernelGGL((chunk_state_kernel<C, NC, F32, MODE, GATE>), dim3(grid), dim3(NTHREADS), 0, s, a);
+  hipLaunchKernelGGL((chunk_state_kernel<C, NC, F32, MODE, GATE>), dim3(grid), dim3(NC * 4), 0, s, a);
   return hipGetLastError();
 }
 
