@@ -79,11 +79,13 @@ __device__ __forceinline__ void load_v(VRaw<C, NC, F32> &r, const StateArgs &a, 
   constexpr int per_tok = NC / 8;
   const size_t tok_stride = (size_t)a.H * D;
   const int cv = MODE == MODE_OUTPUT ? c0 : max(c0 - D, 0);
+  using E = typename std::conditional<F32, float, uint16_t>::type;
+  const E *vb = static_cast<const E *>(a.v) + tok0 + cv;     // uniform
 #pragma unroll
   for (int u = 0; u < VR::NVPT; ++u) {
     const int x = tid + u * VR::NTH;
-    const int tc = min(x / per_tok, nval - 1);
-    r.v[u] = load_q8<F32>(a.v, tok0 + (size_t)tc * tok_stride + cv + (x % per_tok) * 8);
+    const uint32_t tc = (uint32_t)min(x / per_tok, nval - 1);
+    r.v[u] = load_q8<F32>(vb, tc * (uint32_t)tok_stride + (uint32_t)(x % per_tok) * 8u);
   }
 }
 
@@ -207,24 +209,25 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
   // memory operations in flight is known at compile time)
   constexpr int NCOPY = (NBLK + NW - 1) / NW;          // copies per wave and chunk
   auto copy_rec = [&](unsigned char *dst, int chunk, int n0, int n1) __attribute__((always_inline)) {
-    const unsigned char *src = rec_bh + (size_t)chunk * R::bytes + 16 * lane;
+    const unsigned char *src = rec_bh + (size_t)chunk * R::bytes;   // uniform
 #pragma unroll
     for (int n = n0; n < n1; ++n) {
       const int blk = min(wave + NW * n, NBLK - 1);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + (size_t)blk * 1024),
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + (uint32_t)(blk * 1024 + 16 * lane)),
                                        (__attribute__((address_space(3))) void *)(dst + (size_t)blk * 1024), 16, 0, 0);
     }
   };
   // gate logits for the fused epilogue: token 16tb + lr, columns cw + 16j + 4lg .. +3
   auto load_gate = [&](Q4<F32> (&gt)[NT][CBW], int chunk) __attribute__((always_inline)) {
     const int nv = min(C, a.T - chunk * C);
-    const size_t base = tok_base(chunk) + cw + 4 * lg;
+    using E = typename std::conditional<F32, float, uint16_t>::type;
+    const E *gb = static_cast<const E *>(a.gate) + tok_base(chunk) + cw;   // uniform
 #pragma unroll
     for (int tb = 0; tb < NT; ++tb)
 #pragma unroll
       for (int j = 0; j < CBW; ++j) {
-        const int t = min(16 * tb + lr, nv - 1);   // rows past the end are never used
-        gt[tb][j] = load_q4<F32>(a.gate, base + (size_t)t * tok_stride + 16 * j);
+        const uint32_t t = (uint32_t)min(16 * tb + lr, nv - 1);   // rows past the end are never used
+        gt[tb][j] = load_q4<F32>(gb, t * (uint32_t)tok_stride + (uint32_t)(16 * j + 4 * lg));
       }
   };
 
@@ -262,16 +265,22 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
   // c0 + cw + 16j + 4lg .. +3)
   auto store_tile = [&](int chunk, int tb) __attribute__((always_inline)) {
     const int nv = min(C, a.T - chunk * C);
-    const size_t base = tok_base(chunk) + c0 + cw + 4 * lg;
-    const bool bf = a.out_bf16 && !a.raw_out;
+    const size_t base = tok_base(chunk) + c0 + cw;                      // uniform
+    const bool ok = 16 * tb + lr < nv;
+    if (a.out_bf16 && !a.raw_out) {
+      uint16_t *ob = static_cast<uint16_t *>(a.o) + base;
 #pragma unroll
-    for (int j = 0; j < CBW; ++j) {
-      if (16 * tb + lr < nv) {
-        const size_t idx = base + (size_t)(16 * tb + lr) * tok_stride + 16 * j;
-        const float4 x4 = make_float4(op[tb][j][0], op[tb][j][1], op[tb][j][2], op[tb][j][3]);
-        if (bf) store4<true>(a.o, idx, x4);
-        else store4<false>(a.o, idx, x4);
-      }
+      for (int j = 0; j < CBW; ++j)
+        if (ok)
+          store4<true>(ob, (uint32_t)(16 * tb + lr) * (uint32_t)tok_stride + (uint32_t)(16 * j + 4 * lg),
+                       make_float4(op[tb][j][0], op[tb][j][1], op[tb][j][2], op[tb][j][3]));
+    } else {
+      float *ob = static_cast<float *>(a.o) + base;
+#pragma unroll
+      for (int j = 0; j < CBW; ++j)
+        if (ok)
+          *reinterpret_cast<float4 *>(ob + ((uint32_t)(16 * tb + lr) * (uint32_t)tok_stride + (uint32_t)(16 * j + 4 * lg))) =
+              make_float4(op[tb][j][0], op[tb][j][1], op[tb][j][2], op[tb][j][3]);
     }
   };
   // checkpoint: the state after a chunk that ends on a multiple of ckpt_every tokens
@@ -326,28 +335,39 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
 #pragma unroll
       for (int j = 0; j < CBW; ++j) vf[kb][j] = ld_t_split<F32, NC>(sV, 32 * kb, cw + 16 * j, lane);
 
+    // The products run as independent accumulation chains, one per output tile, stepped
+    // together over the contraction blocks, so that consecutive MFMAs do not wait on
+    // each other.
     // ===== U = T V - W S: lane holds U[16tb + 4lg + r][cw + 16j + lr] =====
     f32x4 U[NT][CBW];
 #pragma unroll
-    for (int tb = 0; tb < NT; ++tb) {
-      V8 wf[4], tf[KB];
+    for (int tb = 0; tb < NT; ++tb)
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) wf[kb] = frag(R::oW, tb * 4 + kb);
+      for (int j = 0; j < CBW; ++j) U[tb][j] = zero4();
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) tf[kb] = frag(R::oT, tb * KB + kb);
+    for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-      for (int j = 0; j < CBW; ++j) {
-        f32x4 acc = zero4();
+      for (int tb = 0; tb < NT; ++tb) {
+        const V8 wf = frag(R::oW, tb * 4 + kb);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) acc = Op<F32>::mma(acc, wf[kb], sf[kb][j]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[r] = -acc[r];
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) acc = Op<F32>::mma(acc, tf[kb], vf[kb][j]);
-        U[tb][j] = acc;
+        for (int j = 0; j < CBW; ++j) U[tb][j] = Op<F32>::mma(U[tb][j], wf, sf[kb][j]);
       }
-      copy_rec(rn, nx, tb * NCOPY / NT, (tb + 1) * NCOPY / NT);
+      copy_rec(rn, nx, kb * NCOPY / 4, (kb + 1) * NCOPY / 4);
     }
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb)
+#pragma unroll
+      for (int j = 0; j < CBW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) U[tb][j][r] = -U[tb][j][r];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int tb = 0; tb < NT; ++tb) {
+        const V8 tf = frag(R::oT, tb * KB + kb);
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) U[tb][j] = Op<F32>::mma(U[tb][j], tf, vf[kb][j]);
+      }
     // U as an operand (contraction over tokens; tokens past the chunk are zero)
     V8 uf[KB][CBW];
 #pragma unroll
@@ -355,44 +375,49 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
 #pragma unroll
       for (int j = 0; j < CBW; ++j) uf[kb][j] = frag_from<F32>(U[2 * kb][j], 2 * kb + 1 < NT ? U[2 * kb + 1][j] : zero4());
 
+    // ===== S <- Diag(e^{G_C}) S + Kdec^T U (S as an operand was taken above) =====
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib) {
+      const float4 dec = *reinterpret_cast<const float4 *>(rc + R::oDec + 4 * (16 * ib + 4 * lg));
+#pragma unroll
+      for (int j = 0; j < CBW; ++j) {
+        S[ib][j][0] *= dec.x; S[ib][j][1] *= dec.y; S[ib][j][2] *= dec.z; S[ib][j][3] *= dec.w;
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int ib = 0; ib < 8; ++ib) {
+        const V8 kf = frag(R::oK, ib * KB + kb);
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) S[ib][j] = Op<F32>::mma(S[ib][j], kf, uf[kb][j]);
+      }
+
     // ===== O^T = S^T Qt^T + U^T P^T: lane holds O[16tb + lr][cw + 16j + 4lg + r] =====
     f32x4 O[NT][CBW];
     if constexpr (MODE == MODE_OUTPUT) {
 #pragma unroll
-      for (int tb = 0; tb < NT; ++tb) {
-        V8 qf[4], pf[KB];
+      for (int tb = 0; tb < NT; ++tb)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) qf[kb] = frag(R::oQ, tb * 4 + kb);
+        for (int j = 0; j < CBW; ++j) O[tb][j] = zero4();
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) pf[kb] = frag(R::oP, tb * KB + kb);
+      for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
-        for (int j = 0; j < CBW; ++j) {
-          f32x4 acc = zero4();
+        for (int tb = 0; tb < NT; ++tb) {
+          const V8 qf = frag(R::oQ, tb * 4 + kb);
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) acc = Op<F32>::mma(acc, sf[kb][j], qf[kb]);
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb) acc = Op<F32>::mma(acc, uf[kb][j], pf[kb]);
-          O[tb][j] = acc;
+          for (int j = 0; j < CBW; ++j) O[tb][j] = Op<F32>::mma(O[tb][j], sf[kb][j], qf);
         }
-        if (prev) store_tile(chunk - 1, tb);
+        if (prev && kb < NT) store_tile(chunk - 1, kb);
       }
-    }
-
-    // ===== S <- Diag(e^{G_C}) S + Kdec^T U =====
 #pragma unroll
-    for (int ib = 0; ib < 8; ++ib) {
-      const float4 dec = *reinterpret_cast<const float4 *>(rc + R::oDec + 4 * (16 * ib + 4 * lg));
-      V8 kf[KB];
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) kf[kb] = frag(R::oK, ib * KB + kb);
+        for (int tb = 0; tb < NT; ++tb) {
+          const V8 pf = frag(R::oP, tb * KB + kb);
 #pragma unroll
-      for (int j = 0; j < CBW; ++j) {
-        f32x4 acc = S[ib][j];
-        acc[0] *= dec.x; acc[1] *= dec.y; acc[2] *= dec.z; acc[3] *= dec.w;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) acc = Op<F32>::mma(acc, kf[kb], uf[kb][j]);
-        S[ib][j] = acc;
-      }
+          for (int j = 0; j < CBW; ++j) O[tb][j] = Op<F32>::mma(O[tb][j], uf[kb][j], pf);
+        }
     }
 
     // per-token sums of squares of this wave's columns for the fused RMSNorm
