@@ -386,8 +386,9 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
       };
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
-        Op<F32>::store(reinterpret_cast<T *>(out + R::frag(R::oP, wave * KB + kb, lane)),
-                       frag_from<F32>(pt(2 * kb), pt(2 * kb + 1)));
+        if (R::nz(wave, kb))                           // blocks above the diagonal are not stored
+          Op<F32>::store(reinterpret_cast<T *>(out + R::frag(R::oP, R::tri(wave, kb), lane)),
+                         frag_from<F32>(pt(2 * kb), pt(2 * kb + 1)));
     }
 
     // Kdec^T fragments: Kdec = KF * prod_{m>w} D_m, read transposed from KF.  Lane
@@ -466,12 +467,20 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
         w0 = Op<F32>::mma(w0, ld_t<F32, D>(sKT, 32 * kc, 32 * kb, lane), b);
         w1 = Op<F32>::mma(w1, ld_t<F32, D>(sKT, 32 * kc, 32 * kb + 16, lane), b);
       }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {                   // stored negated
+        w0[r] = -w0[r];
+        w1[r] = -w1[r];
+      }
       Op<F32>::store(reinterpret_cast<T *>(out + R::frag(R::oW, f, lane)), frag_from<F32>(w0, w1));
     }
     // T fragments and the chunk decay
-    for (int f = wave; f < R::nT; f += 4)
-      Op<F32>::store(reinterpret_cast<T *>(out + R::frag(R::oT, f, lane)),
-                     ld_t_split<F32, C>(sTt, 32 * (f % KB), 16 * (f / KB), lane));
+    for (int f = wave; f < NT * KB; f += 4) {
+      const int tb = f / KB, kb = f % KB;
+      if (R::nz(tb, kb))                               // blocks above the diagonal are not stored
+        Op<F32>::store(reinterpret_cast<T *>(out + R::frag(R::oT, R::tri(tb, kb), lane)),
+                       ld_t_split<F32, C>(sTt, 32 * kb, 16 * tb, lane));
+    }
     if (tid < D / 4)
       reinterpret_cast<float4 *>(out + R::oDec)[tid] = reinterpret_cast<const float4 *>(sDecay)[tid];
   }

@@ -129,6 +129,41 @@ __device__ __forceinline__ float q4_at(const Q4<F32> &x, int e) {
   }
 }
 
+// Byte offsets (within a record) of the operand fragments one chunk step reads, in
+// the order it reads them: -W (key block outer, token tile inner), T, Kdec^T, then for
+// outputs Qt and P.  Blocks of T and P above the diagonal are zero and not stored.
+template <int C, bool F32, bool OUT>
+struct SeqFrags {
+  using R = Rec<C, F32>;
+  static constexpr int NT = C / 16, KB = R::KB;
+  struct List {
+    int off[R::nW + R::nT + R::nK + R::nQ + R::nP];
+    int n;
+  };
+  static constexpr List make() {
+    List l{};
+    int n = 0;
+    for (int kb = 0; kb < 4; ++kb)
+      for (int tb = 0; tb < NT; ++tb) l.off[n++] = (int)(R::oW + (size_t)(tb * 4 + kb) * R::FRAG);
+    for (int kb = 0; kb < KB; ++kb)
+      for (int tb = 0; tb < NT; ++tb)
+        if (R::nz(tb, kb)) l.off[n++] = (int)(R::oT + (size_t)R::tri(tb, kb) * R::FRAG);
+    for (int kb = 0; kb < KB; ++kb)
+      for (int ib = 0; ib < 8; ++ib) l.off[n++] = (int)(R::oK + (size_t)(ib * KB + kb) * R::FRAG);
+    if (OUT) {
+      for (int kb = 0; kb < 4; ++kb)
+        for (int tb = 0; tb < NT; ++tb) l.off[n++] = (int)(R::oQ + (size_t)(tb * 4 + kb) * R::FRAG);
+      for (int kb = 0; kb < KB; ++kb)
+        for (int tb = 0; tb < NT; ++tb)
+          if (R::nz(tb, kb)) l.off[n++] = (int)(R::oP + (size_t)R::tri(tb, kb) * R::FRAG);
+    }
+    l.n = n;
+    return l;
+  }
+  static constexpr List seq = make();
+  static constexpr int n = seq.n;
+};
+
 // GATE: the output pass of a whole head (NC = 128) with the fused RMSNorm and gate
 template <int C, int NC, bool F32, int MODE, bool GATE>
 __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
@@ -143,14 +178,17 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
   constexpr int CBW = NCW / 16;                        // 16-column blocks per wave
   static_assert(!GATE || (MODE == MODE_OUTPUT && NC == D), "the fused epilogue needs whole heads");
   constexpr int VS = (MODE == MODE_TRANSITION ? 2 * D : D) / NC;   // workgroups per unit
-  constexpr int NBLK = (int)(R::bytes / 1024);         // record size in KiB
-  // Two record buffers, the chunk's values and the norm partials are separate LDS
-  // objects, so the compiler sees that reads of one buffer do not depend on the
-  // asynchronous copy in flight into the other.
-  __shared__ __align__(16) unsigned char recA[R::bytes];
-  __shared__ __align__(16) unsigned char recB[R::bytes];
-  __shared__ __align__(16) T sV[KC * NC];              // V [t][c] (rows >= C zero)
-  __shared__ float sNorm[GATE ? NW * C : 1];           // per-wave sums of squares
+  // KiB of the record this pass copies (the state map needs only its prefix)
+  constexpr int NBLK = (int)((MODE == MODE_TRANSITION ? R::trans : R::bytes) / 1024);
+  // Records, values and norm partials are double buffered (chunks alternate), each
+  // buffer a separate LDS object, so the compiler sees that reads of one buffer do not
+  // depend on the asynchronous copy in flight into the other.
+  __shared__ __align__(16) unsigned char recA[NBLK * 1024];
+  __shared__ __align__(16) unsigned char recB[NBLK * 1024];
+  __shared__ __align__(16) T sVA[KC * NC];             // V [t][c] (rows >= C zero)
+  __shared__ __align__(16) T sVB[KC * NC];
+  __shared__ __align__(16) float sNormA[GATE ? C * NW : 1];   // per-token, per-wave sums of squares
+  __shared__ __align__(16) float sNormB[GATE ? C * NW : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -178,7 +216,7 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
 
   // V rows past the chunk stay zero (only when KC > C)
   if constexpr (KC > C) {
-    for (int x = tid; x < (KC - C) * NC; x += NTH) sV[C * NC + x] = T(0);
+    for (int x = tid; x < (KC - C) * NC; x += NTH) sVA[C * NC + x] = sVB[C * NC + x] = T(0);
   }
 
   // ---- initial state: S[ib][j] holds rows 16ib + 4lg + r, column c0 + cw + 16j + lr
@@ -237,11 +275,13 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
   // Pipeline.  Within one chunk no register loaded during that chunk is consumed:
   // with loads, stores and LDS copies in flight together the compiler can only wait
   // for all of them, so every wait happens at the top of a chunk, where the record
-  // copy has to be complete anyway.  Per chunk n: the record of n+1 is copied, the
-  // gate of n+1 is loaded, the outputs of n-1 are stored, and in the middle of the
-  // chunk the values of n+1 (loaded during n-1) go to LDS and those of n+2 are loaded.
+  // copy has to be complete anyway.  Per chunk n, after the one barrier of the step:
+  // the norm and gate of chunk n-1 are applied (its per-wave sums of squares were
+  // written at the end of n-1), the gate of n is loaded, the values of n+1 (loaded
+  // during n-1) go to the other V buffer and those of n+2 are loaded, the record of
+  // n+1 is copied, and the outputs of n-1 are stored between the products.
   VRaw<C, NC, F32> vr;
-  Q4<F32> gc[NT][CBW], gn[NT][CBW];
+  Q4<F32> gq[NT][CBW];                                 // gate logits of one chunk
   f32x4 op[NT][CBW];                                   // outputs of the previous chunk
   float wv[CBW][4];                                    // RMSNorm weights of this wave's columns
   if constexpr (GATE) {
@@ -252,14 +292,33 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
   }
   const int ch_last = ch_end - 1;
   load_v<C, NC, F32, MODE>(vr, a, tok_base(ch_begin), min(C, a.T - ch_begin * C), c0, tid);
-  if constexpr (GATE) load_gate(gn, ch_begin);
   copy_rec(recA, ch_begin, 0, NCOPY);
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  store_v<C, NC, F32, MODE>(sV, vr, min(C, a.T - ch_begin * C), c0, tid);
+  store_v<C, NC, F32, MODE>(sVA, vr, min(C, a.T - ch_begin * C), c0, tid);
   {
     const int n1 = min(ch_begin + 1, ch_last);
     load_v<C, NC, F32, MODE>(vr, a, tok_base(n1), min(C, a.T - n1 * C), c0, tid);
   }
+
+  // per-head RMSNorm over the 128 value columns, then the sigmoid gate, applied to the
+  // raw outputs op of one chunk, with that chunk's sums of squares and gate logits
+  auto norm_gate = [&](const float *sn) __attribute__((always_inline)) {
+#pragma unroll
+    for (int tb = 0; tb < NT; ++tb) {
+      const int t = 16 * tb + lr;
+      float tot = 0.f;
+#pragma unroll
+      for (int w4 = 0; w4 < NW / 4; ++w4) {
+        const float4 x = *reinterpret_cast<const float4 *>(sn + t * NW + 4 * w4);
+        tot += (x.x + x.y) + (x.z + x.w);
+      }
+      const float inv = rsqrtf(tot * (1.0f / D) + a.eps);
+#pragma unroll
+      for (int j = 0; j < CBW; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) op[tb][j][r] *= inv * wv[j][r] * sigmoidf_(q4_at<F32>(gq[tb][j], r));
+    }
+  };
 
   // outputs of token tile tb of one chunk (lane: token 16tb + lr, columns
   // c0 + cw + 16j + 4lg .. +3)
@@ -299,30 +358,54 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
     }
   };
 
-  // one chunk, reading record buffer BUF (recA or recB) and filling the other
+  // one chunk, reading record and value buffers BUF (A or B) and filling the others
   auto step = [&](auto bufc, int chunk) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
     unsigned char *rc = BUF == 0 ? recA : recB;
     unsigned char *rn = BUF == 0 ? recB : recA;
+    const T *sV = BUF == 0 ? sVA : sVB;
+    T *sVn = BUF == 0 ? sVB : sVA;
     __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0): this wave's loads landed
     __syncthreads();                                   // every wave's; V of this chunk visible
 
+    const bool prev = MODE == MODE_OUTPUT && chunk > ch_begin;
     if constexpr (GATE) {
-#pragma unroll
-      for (int tb = 0; tb < NT; ++tb)
-#pragma unroll
-        for (int j = 0; j < CBW; ++j) gc[tb][j] = gn[tb][j];
+      if (prev) norm_gate(BUF == 0 ? sNormB : sNormA);
+      load_gate(gq, chunk);
     }
     const int nx = min(chunk + 1, ch_last);            // the last chunk reloads its own
-    if constexpr (GATE) load_gate(gn, nx);
-    const bool prev = MODE == MODE_OUTPUT && chunk > ch_begin;
+    {                                                  // values of chunk+1 (loaded a chunk ago)
+      store_v<C, NC, F32, MODE>(sVn, vr, min(C, a.T - nx * C), c0, tid);
+      const int n2 = min(chunk + 2, ch_last);
+      load_v<C, NC, F32, MODE>(vr, a, tok_base(n2), min(C, a.T - n2 * C), c0, tid);
+    }
     if (prev) store_ckpt(chunk - 1);
-    // The record copy and the previous chunk's output stores are issued in pieces
-    // between the products below, so that the memory pipeline works while the
-    // matrix cores do.
 
-    auto frag = [&](size_t off, int f) __attribute__((always_inline)) {
-      return Op<F32>::load(reinterpret_cast<const T *>(rc + R::frag(off, f, lane)));
+    // Record fragments are read from LDS through a ring of PF registers, PF fragments
+    // ahead of the product that consumes them, in the order the products below take
+    // them (SeqFrags), so that LDS latency overlaps the matrix cores.
+    using SF = SeqFrags<C, F32, MODE == MODE_OUTPUT>;
+    constexpr int PF = SF::n < 4 ? SF::n : 4;
+    auto fetch = [&](int i) __attribute__((always_inline)) {
+      return Op<F32>::load(reinterpret_cast<const T *>(rc + SF::seq.off[i] + lane * 8 * sizeof(T)));
+    };
+    // The next chunk's record copy.  While an asynchronous copy into LDS is in flight
+    // the compiler waits for all outstanding LDS reads at every use, which defeats the
+    // read-ahead, so the outputs pass issues it after its last fragment read; the state
+    // map pass has less work after that point and issues it first.
+    if constexpr (MODE == MODE_TRANSITION) {
+      copy_rec(rn, nx, 0, NCOPY);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    V8 ring[PF];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) ring[i] = fetch(i);
+    auto take = [&](int i) __attribute__((always_inline)) {
+      const V8 f = ring[i % PF];
+      if (i + PF < SF::n) ring[i % PF] = fetch(i + PF);
+      if (MODE == MODE_OUTPUT && i + PF == SF::n - 1) copy_rec(rn, nx, 0, NCOPY);
+      __builtin_amdgcn_sched_barrier(0);             // keep the read PF products ahead
+      return f;
     };
     // S and V as operands (contraction over key channels / tokens, split order)
     V8 sf[4][CBW], vf[KB][CBW];
@@ -338,7 +421,8 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
     // The products run as independent accumulation chains, one per output tile, stepped
     // together over the contraction blocks, so that consecutive MFMAs do not wait on
     // each other.
-    // ===== U = T V - W S: lane holds U[16tb + 4lg + r][cw + 16j + lr] =====
+    int fi = 0;                                        // next fragment of the sequence
+    // ===== U = T V + (-W) S: lane holds U[16tb + 4lg + r][cw + 16j + lr] =====
     f32x4 U[NT][CBW];
 #pragma unroll
     for (int tb = 0; tb < NT; ++tb)
@@ -348,23 +432,17 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
     for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
       for (int tb = 0; tb < NT; ++tb) {
-        const V8 wf = frag(R::oW, tb * 4 + kb);
+        const V8 wf = take(fi++);
 #pragma unroll
         for (int j = 0; j < CBW; ++j) U[tb][j] = Op<F32>::mma(U[tb][j], wf, sf[kb][j]);
       }
-      copy_rec(rn, nx, kb * NCOPY / 4, (kb + 1) * NCOPY / 4);
     }
-#pragma unroll
-    for (int tb = 0; tb < NT; ++tb)
-#pragma unroll
-      for (int j = 0; j < CBW; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) U[tb][j][r] = -U[tb][j][r];
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int tb = 0; tb < NT; ++tb) {
-        const V8 tf = frag(R::oT, tb * KB + kb);
+        if (!R::nz(tb, kb)) continue;                  // T is lower triangular
+        const V8 tf = take(fi++);
 #pragma unroll
         for (int j = 0; j < CBW; ++j) U[tb][j] = Op<F32>::mma(U[tb][j], tf, vf[kb][j]);
       }
@@ -388,7 +466,7 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
       for (int ib = 0; ib < 8; ++ib) {
-        const V8 kf = frag(R::oK, ib * KB + kb);
+        const V8 kf = take(fi++);
 #pragma unroll
         for (int j = 0; j < CBW; ++j) S[ib][j] = Op<F32>::mma(S[ib][j], kf, uf[kb][j]);
       }
@@ -404,7 +482,7 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
       for (int kb = 0; kb < 4; ++kb) {
 #pragma unroll
         for (int tb = 0; tb < NT; ++tb) {
-          const V8 qf = frag(R::oQ, tb * 4 + kb);
+          const V8 qf = take(fi++);
 #pragma unroll
           for (int j = 0; j < CBW; ++j) O[tb][j] = Op<F32>::mma(O[tb][j], sf[kb][j], qf);
         }
@@ -414,14 +492,22 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int tb = 0; tb < NT; ++tb) {
-          const V8 pf = frag(R::oP, tb * KB + kb);
+          if (!R::nz(tb, kb)) continue;                // P is lower triangular
+          const V8 pf = take(fi++);
 #pragma unroll
           for (int j = 0; j < CBW; ++j) O[tb][j] = Op<F32>::mma(O[tb][j], uf[kb][j], pf);
         }
     }
 
+    if constexpr (MODE == MODE_OUTPUT) {
+#pragma unroll
+      for (int tb = 0; tb < NT; ++tb)
+#pragma unroll
+        for (int j = 0; j < CBW; ++j) op[tb][j] = O[tb][j];
+    }
     // per-token sums of squares of this wave's columns for the fused RMSNorm
     if constexpr (GATE) {
+      float *sn = BUF == 0 ? sNormA : sNormB;
 #pragma unroll
       for (int tb = 0; tb < NT; ++tb) {
         float ss = 0.f;
@@ -431,45 +517,7 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
           for (int r = 0; r < 4; ++r) ss += O[tb][j][r] * O[tb][j][r];
         ss += __shfl_xor(ss, 16, 64);
         ss += __shfl_xor(ss, 32, 64);
-        if (lg == 0) sNorm[wave * C + 16 * tb + lr] = ss;
-      }
-    }
-    // Norm partials visible and every wave done with this chunk's V.  A barrier without
-    // a memory fence: a fence would wait for the record copy in flight.
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0): own LDS accesses done
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    {                                                  // values of chunk+1 (loaded a chunk ago)
-      const int n1 = min(chunk + 1, ch_last);
-      store_v<C, NC, F32, MODE>(sV, vr, min(C, a.T - n1 * C), c0, tid);
-    }
-    {
-      const int n2 = min(chunk + 2, ch_last);
-      load_v<C, NC, F32, MODE>(vr, a, tok_base(n2), min(C, a.T - n2 * C), c0, tid);
-    }
-
-    if constexpr (MODE == MODE_OUTPUT) {
-      if constexpr (GATE) {
-        // per-head RMSNorm over the 128 value columns, then the sigmoid gate
-#pragma unroll
-        for (int tb = 0; tb < NT; ++tb) {
-          const int t = 16 * tb + lr;
-          float tot = 0.f;
-#pragma unroll
-          for (int w = 0; w < NW; ++w) tot += sNorm[w * C + t];
-          const float inv = rsqrtf(tot * (1.0f / D) + a.eps);
-#pragma unroll
-          for (int j = 0; j < CBW; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              op[tb][j][r] = O[tb][j][r] * inv * wv[j][r] * sigmoidf_(q4_at<F32>(gc[tb][j], r));
-        }
-      } else {
-#pragma unroll
-        for (int tb = 0; tb < NT; ++tb)
-#pragma unroll
-          for (int j = 0; j < CBW; ++j) op[tb][j] = O[tb][j];
+        if (lg == 0) sn[(16 * tb + lr) * NW + wave] = ss;
       }
     }
   };
@@ -478,6 +526,9 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
     if (chunk + 1 < ch_end) step(std::integral_constant<int, 1>{}, chunk + 1);
   }
   if constexpr (MODE == MODE_OUTPUT) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);                // gate of the last chunk
+    __syncthreads();                                   // its sums of squares
+    if constexpr (GATE) norm_gate(((ch_last - ch_begin) & 1) == 0 ? sNormA : sNormB);
 #pragma unroll
     for (int tb = 0; tb < NT; ++tb) store_tile(ch_last, tb);
     store_ckpt(ch_last);

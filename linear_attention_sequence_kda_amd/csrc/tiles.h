@@ -247,8 +247,16 @@ __device__ __forceinline__ void f8_from(float *dst, float4 a, float4 b) {
 // Every matrix is stored as whole MFMA operand fragments with the contraction index
 // in split order (see ld_n_split): fragment f holds 512 elements, lane l's 8 elements
 // at f * 512 + 8 l, so a wave reads a fragment with one 16-byte (fp16) or 32-byte
-// (fp32) access per lane.  The record size is a whole number of KiB, so that it is
-// copied to LDS in 1 KiB wave-wide pieces.
+// (fp32) access per lane.
+//   -W      [t][i]   token tile t, key block i (stored negated: U = T V + (-W) S)
+//   T       [t][j]   token tile t, token block j; only blocks on or below the diagonal
+//   Kdec^T  [i][j]   key tile i, token block j
+//   e^{G_C}          per key channel, fp32
+//   Qt      [t][i]
+//   P       [t][j]   only blocks on or below the diagonal
+// The state map of a chunk needs only the first four (the prefix of `trans` bytes);
+// the outputs need all.  Both sizes are whole KiB, so the record is copied to LDS in
+// 1 KiB wave-wide pieces.
 // ---------------------------------------------------------------------------
 template <int C, bool F32>
 struct Rec {
@@ -256,19 +264,39 @@ struct Rec {
   static constexpr int NT = C / 16;                   // 16-token tiles
   static constexpr int KB = (C < 32 ? 32 : C) / 32;   // 32-token contraction blocks
   static constexpr size_t FRAG = 512 * sizeof(T);
-  // fragment counts: rows x contraction blocks
-  static constexpr int nW = NT * 4;    // W      [t][i]    rows t,  k = key channel
-  static constexpr int nQ = NT * 4;    // Qt     [t][i]
-  static constexpr int nP = NT * KB;   // P      [t][j]    rows t,  k = token
-  static constexpr int nT = NT * KB;   // T      [t][j]
-  static constexpr int nK = 8 * KB;    // Kdec^T [i][t]    rows i,  k = token
+  // fragment (token tile tb, token block kb) is zero when the block lies wholly above
+  // the diagonal of a lower triangular C x C matrix
+  static constexpr bool nz(int tb, int kb) { return 32 * kb <= 16 * tb + 15; }
+  static constexpr int count_tri() {
+    int n = 0;
+    for (int tb = 0; tb < NT; ++tb)
+      for (int kb = 0; kb < KB; ++kb) n += nz(tb, kb) ? 1 : 0;
+    return n;
+  }
+  // position of a nonzero (tb, kb) fragment of T or P among the stored ones
+  static constexpr int tri(int tb, int kb) {
+    int n = 0;
+    for (int t = 0; t < NT; ++t)
+      for (int k = 0; k < KB; ++k) {
+        if (t == tb && k == kb) return n;
+        n += nz(t, k) ? 1 : 0;
+      }
+    return -1;
+  }
+  static constexpr int nW = NT * 4;
+  static constexpr int nT = count_tri();
+  static constexpr int nK = 8 * KB;
+  static constexpr int nQ = NT * 4;
+  static constexpr int nP = count_tri();
+  static constexpr size_t kib(size_t x) { return (x + 1023) & ~size_t(1023); }
   static constexpr size_t oW = 0;
-  static constexpr size_t oQ = oW + nW * FRAG;
-  static constexpr size_t oP = oQ + nQ * FRAG;
-  static constexpr size_t oT = oP + nP * FRAG;
+  static constexpr size_t oT = oW + nW * FRAG;
   static constexpr size_t oK = oT + nT * FRAG;
-  static constexpr size_t oDec = oK + nK * FRAG;      // e^{G_C} per key channel, fp32
-  static constexpr size_t bytes = (oDec + D * 4 + 1023) & ~size_t(1023);
+  static constexpr size_t oDec = oK + nK * FRAG;
+  static constexpr size_t trans = kib(oDec + D * 4);
+  static constexpr size_t oQ = trans;
+  static constexpr size_t oP = oQ + nQ * FRAG;
+  static constexpr size_t bytes = kib(oP + nP * FRAG);
   static __device__ __forceinline__ size_t frag(size_t off, int f, int lane) {
     return off + (size_t)f * FRAG + (size_t)lane * 8 * sizeof(T);
   }

@@ -98,8 +98,11 @@ def test_prefill_validation_errors():
     assert _call(d) == kda.KDA_ERR_WORKSPACE
     n = C.c_size_t(0)
     assert lib.kda_prefill_workspace_size(C.byref(d), C.byref(n)) == kda.KDA_OK
-    # per-chunk records (2 chunks x 8 heads) + maps and entering states of 2 segments
-    assert n.value >= 2 * 4 * 2 * 66048 + 2 * 4 * 2 * 3 * 128 * 128 * 4
+    # per-chunk records (2 chunks x 8 heads; a 64-token record holds W, Kdec and Qt,
+    # 64 x 128 fp16 each, the 6 stored 16x32 blocks of T and of P, and 128 fp32
+    # decays) + maps and entering states of 2 segments
+    rec = 3 * 64 * 128 * 2 + 2 * 6 * 16 * 32 * 2 + 128 * 4
+    assert n.value >= 2 * 4 * 2 * rec + 2 * 4 * 2 * 3 * 128 * 128 * 4
     d.workspace, d.workspace_bytes = FAKE + (1 << 36), n.value - 1
     assert _call(d) == kda.KDA_ERR_WORKSPACE
     assert lib.kda_prefill_workspace_size(C.byref(_desc()), None) == kda.KDA_ERR_NULL
