@@ -47,11 +47,24 @@ struct StateArgs {
   int n_units;        // B * H * n_seg
 };
 
-// value columns of one chunk for this workgroup's slice: groups of 8 columns, token-major
-template <int C, int NC, bool F32>
+// Workgroup shape for NC state columns: up to 8 waves, 16 or 32 columns each.  VC
+// value columns come with them: all NC for outputs; for a state map ([A | B], 2D
+// columns) only the D columns of the B part carry values.
+template <int NC, int MODE>
+struct Shape {
+  static constexpr int NW = NC / 16 < 8 ? NC / 16 : 8;
+  static constexpr int NTH = NW * 64;
+  static constexpr int NCW = NC / NW;                  // state columns per wave
+  static constexpr int VC = MODE == MODE_OUTPUT ? NC : D;
+  static constexpr int VOFF = MODE == MODE_OUTPUT ? 0 : D;   // first state column with values
+};
+
+// value columns of one chunk for this workgroup: groups of 8 columns, token-major
+template <int C, int NC, bool F32, int MODE>
 struct VRaw {
-  static constexpr int NTH = NC * 4;                   // threads of the workgroup (NC / 16 waves)
-  static constexpr int NVG = C * NC / 8;
+  static constexpr int NTH = Shape<NC, MODE>::NTH;
+  static constexpr int VC = Shape<NC, MODE>::VC;
+  static constexpr int NVG = C * VC / 8;
   static constexpr int NVPT = (NVG + NTH - 1) / NTH;
   Q8<F32> v[NVPT];
 };
@@ -73,12 +86,12 @@ __device__ __forceinline__ Q8<F32> keep_if(Q8<F32> x, bool ok) {
 // the A part of a transition map, which carries no value) are zeroed when stored to
 // LDS, so that a load is never consumed right after it is issued.
 template <int C, int NC, bool F32, int MODE>
-__device__ __forceinline__ void load_v(VRaw<C, NC, F32> &r, const StateArgs &a, size_t tok0, int nval,
+__device__ __forceinline__ void load_v(VRaw<C, NC, F32, MODE> &r, const StateArgs &a, size_t tok0, int nval,
                                        int c0, int tid) {
-  using VR = VRaw<C, NC, F32>;
-  constexpr int per_tok = NC / 8;
+  using VR = VRaw<C, NC, F32, MODE>;
+  constexpr int per_tok = VR::VC / 8;
   const size_t tok_stride = (size_t)a.H * D;
-  const int cv = MODE == MODE_OUTPUT ? c0 : max(c0 - D, 0);
+  const int cv = MODE == MODE_OUTPUT ? c0 : 0;
   using E = typename std::conditional<F32, float, uint16_t>::type;
   const E *vb = static_cast<const E *>(a.v) + tok0 + cv;     // uniform
 #pragma unroll
@@ -90,21 +103,19 @@ __device__ __forceinline__ void load_v(VRaw<C, NC, F32> &r, const StateArgs &a, 
 }
 
 template <int C, int NC, bool F32, int MODE>
-__device__ __forceinline__ void store_v(typename Op<F32>::T *sV, const VRaw<C, NC, F32> &r, int nval, int c0,
+__device__ __forceinline__ void store_v(typename Op<F32>::T *sV, const VRaw<C, NC, F32, MODE> &r, int nval,
                                         int tid) {
-  using VR = VRaw<C, NC, F32>;
-  constexpr int per_tok = NC / 8;
-  // transition mode: virtual columns < D form the A part of the map and carry no value
-  const bool has_v = MODE == MODE_OUTPUT || c0 >= D;
+  using VR = VRaw<C, NC, F32, MODE>;
+  constexpr int per_tok = VR::VC / 8;
 #pragma unroll
   for (int u = 0; u < VR::NVPT; ++u) {
     const int x = tid + u * VR::NTH;
     if (VR::NVG % VR::NTH == 0 || x < VR::NVG) {
-      const Q8<F32> q = keep_if<F32>(r.v[u], has_v && x / per_tok < nval);
+      const Q8<F32> q = keep_if<F32>(r.v[u], x / per_tok < nval);
       float vv[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) vv[e] = q8_at<F32>(q, e);
-      st8<F32, NC>(sV, x / per_tok, (x % per_tok) * 8, vv);
+      st8<F32, VR::VC>(sV, x / per_tok, (x % per_tok) * 8, vv);
     }
   }
 }
@@ -166,16 +177,17 @@ struct SeqFrags {
 
 // GATE: the output pass of a whole head (NC = 128) with the fused RMSNorm and gate
 template <int C, int NC, bool F32, int MODE, bool GATE>
-__global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
+__global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(StateArgs a) {
   using R = Rec<C, F32>;
   using T = typename Op<F32>::T;
   using V8 = typename Op<F32>::V8;
   constexpr int KC = C < 32 ? 32 : C;
   constexpr int KB = R::KB, NT = C / 16;
-  constexpr int NW = NC / 16;                          // waves: one 16-column block each,
-  constexpr int NTH = NW * 64;                         // two waves per SIMD for NC = 128
-  constexpr int NCW = 16;                              // state columns per wave
+  using SH = Shape<NC, MODE>;
+  constexpr int NW = SH::NW, NTH = SH::NTH;            // two waves per SIMD for NC >= 128
+  constexpr int NCW = SH::NCW;                         // state columns per wave
   constexpr int CBW = NCW / 16;                        // 16-column blocks per wave
+  constexpr int VC = SH::VC;                           // value columns in LDS
   static_assert(!GATE || (MODE == MODE_OUTPUT && NC == D), "the fused epilogue needs whole heads");
   constexpr int VS = (MODE == MODE_TRANSITION ? 2 * D : D) / NC;   // workgroups per unit
   // KiB of the record this pass copies (the state map needs only its prefix)
@@ -185,12 +197,14 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
   // depend on the asynchronous copy in flight into the other.
   __shared__ __align__(16) unsigned char recA[NBLK * 1024];
   __shared__ __align__(16) unsigned char recB[NBLK * 1024];
-  __shared__ __align__(16) T sVA[KC * NC];             // V [t][c] (rows >= C zero)
-  __shared__ __align__(16) T sVB[KC * NC];
+  __shared__ __align__(16) T sVA[KC * VC];             // V [t][c] (rows >= C zero)
+  __shared__ __align__(16) T sVB[KC * VC];
   __shared__ __align__(16) float sNormA[GATE ? C * NW : 1];   // per-token, per-wave sums of squares
   __shared__ __align__(16) float sNormB[GATE ? C * NW : 1];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: branches on it are scalar (MFMAs ignore the lane mask,
+  // so a product skipped by a wave must be skipped by a real branch)
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lr = lane & 15, lg = lane >> 4;
 
   // XCD-aware placement: consecutive workgroup ids go to different XCDs, so the
@@ -216,7 +230,7 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
 
   // V rows past the chunk stay zero (only when KC > C)
   if constexpr (KC > C) {
-    for (int x = tid; x < (KC - C) * NC; x += NTH) sVA[C * NC + x] = sVB[C * NC + x] = T(0);
+    for (int x = tid; x < (KC - C) * VC; x += NTH) sVA[C * VC + x] = sVB[C * VC + x] = T(0);
   }
 
   // ---- initial state: S[ib][j] holds rows 16ib + 4lg + r, column c0 + cw + 16j + lr
@@ -280,7 +294,7 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
   // written at the end of n-1), the gate of n is loaded, the values of n+1 (loaded
   // during n-1) go to the other V buffer and those of n+2 are loaded, the record of
   // n+1 is copied, and the outputs of n-1 are stored between the products.
-  VRaw<C, NC, F32> vr;
+  VRaw<C, NC, F32, MODE> vr;
   Q4<F32> gq[NT][CBW];                                 // gate logits of one chunk
   f32x4 op[NT][CBW];                                   // outputs of the previous chunk
   float wv[CBW][4];                                    // RMSNorm weights of this wave's columns
@@ -294,7 +308,7 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
   load_v<C, NC, F32, MODE>(vr, a, tok_base(ch_begin), min(C, a.T - ch_begin * C), c0, tid);
   copy_rec(recA, ch_begin, 0, NCOPY);
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  store_v<C, NC, F32, MODE>(sVA, vr, min(C, a.T - ch_begin * C), c0, tid);
+  store_v<C, NC, F32, MODE>(sVA, vr, min(C, a.T - ch_begin * C), tid);
   {
     const int n1 = min(ch_begin + 1, ch_last);
     load_v<C, NC, F32, MODE>(vr, a, tok_base(n1), min(C, a.T - n1 * C), c0, tid);
@@ -375,7 +389,7 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
     }
     const int nx = min(chunk + 1, ch_last);            // the last chunk reloads its own
     {                                                  // values of chunk+1 (loaded a chunk ago)
-      store_v<C, NC, F32, MODE>(sVn, vr, min(C, a.T - nx * C), c0, tid);
+      store_v<C, NC, F32, MODE>(sVn, vr, min(C, a.T - nx * C), tid);
       const int n2 = min(chunk + 2, ch_last);
       load_v<C, NC, F32, MODE>(vr, a, tok_base(n2), min(C, a.T - n2 * C), c0, tid);
     }
@@ -408,15 +422,19 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
       return f;
     };
     // S and V as operands (contraction over key channels / tokens, split order)
-    V8 sf[4][CBW], vf[KB][CBW];
+    V8 sf[4][CBW], vf[KB][CBW] = {};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < CBW; ++j) sf[kb][j] = frag_from<F32>(S[2 * kb][j], S[2 * kb + 1][j]);
+    // the A part of a state map (columns < D) carries no values: no T V product there
+    const bool has_v = MODE == MODE_OUTPUT || c0 + cw >= D;        // wave-uniform
+    if (has_v) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int j = 0; j < CBW; ++j) vf[kb][j] = ld_t_split<F32, NC>(sV, 32 * kb, cw + 16 * j, lane);
+        for (int j = 0; j < CBW; ++j) vf[kb][j] = ld_t_split<F32, VC>(sV, 32 * kb, cw - SH::VOFF + 16 * j, lane);
+    }
 
     // The products run as independent accumulation chains, one per output tile, stepped
     // together over the contraction blocks, so that consecutive MFMAs do not wait on
@@ -443,8 +461,10 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
       for (int tb = 0; tb < NT; ++tb) {
         if (!R::nz(tb, kb)) continue;                  // T is lower triangular
         const V8 tf = take(fi++);
+        if (has_v) {
 #pragma unroll
-        for (int j = 0; j < CBW; ++j) U[tb][j] = Op<F32>::mma(U[tb][j], tf, vf[kb][j]);
+          for (int j = 0; j < CBW; ++j) U[tb][j] = Op<F32>::mma(U[tb][j], tf, vf[kb][j]);
+        }
       }
     // U as an operand (contraction over tokens; tokens past the chunk are zero)
     V8 uf[KB][CBW];
@@ -564,8 +584,17 @@ __global__ __launch_bounds__(NC * 4, 1) void chunk_state_kernel(StateArgs a) {
 // associative scan of segment maps: S_in[0] = S0, S_in[s+1] = A_s S_in[s] + B_s
 // ("xhh.club" structure entry: context parallelism by an associative prefix scan; the
 // states entering later segments are composed, never summed).  One workgroup per
-// (sequence, head, 16-column block); the map product runs as fp32 MFMA.
+// (sequence, head, 16-column block); the map product runs as fp32 MFMA.  The eight
+// column blocks of a unit share an XCD (ids equal modulo 8), so each map is fetched
+// from memory once into that XCD's L2.  The next map's rows are loaded while the
+// current product runs; each 16x16 result tile accumulates in four independent
+// chains over the 128-long contraction.
 // ---------------------------------------------------------------------------
+struct MapRows {
+  float4 a[2][8];     // A rows (2 tiles), contraction 32lg .. 32lg + 31
+  float b[2][4];      // B at rows 4lg + r of each tile, this lane's column
+};
+
 __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *__restrict__ maps,
                                                            const float *__restrict__ S0,
                                                            float *__restrict__ sin, int n_seg,
@@ -573,7 +602,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *__restr
   __shared__ __align__(16) float sXt[16][D + 4];      // current state block, transposed [n][i]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
-  const int bh = blockIdx.x / (D / 16), cb = blockIdx.x % (D / 16);
+  const int xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
+  const int cb = rest % (D / 16), bh = (rest / (D / 16)) * 8 + xcd;
   if (bh >= n_bh) return;
   const int c0 = cb * 16;
   // S_in[0] = S0 (or zeros)
@@ -583,27 +613,40 @@ __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *__restr
     sXt[n][i] = v;
     sin[((size_t)bh * n_seg) * D * D + (size_t)i * D + c0 + n] = v;
   }
-  __syncthreads();
-  for (int s = 0; s + 1 < n_seg; ++s) {
+  // wave w computes rows 32w .. 32w + 31 (two 16-row tiles)
+  auto load_map = [&](MapRows &m, int s) __attribute__((always_inline)) {
     const float *A = maps + ((size_t)bh * n_seg + s) * D * (2 * D);
-    f32x4 acc[2];
-    // wave w computes rows 32w..32w+31 (two 16-row tiles); lane group g supplies
-    // contraction indices 32g .. 32g+31 (one per MFMA).
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-      const int i = (2 * wave + it) * 16 + lr;
-      f32x4 c = zero4();
-      const float *arow = A + (size_t)i * (2 * D) + 32 * lg;
+      const int row0 = (2 * wave + it) * 16;
+      const float *arow = A + (size_t)(row0 + lr) * (2 * D) + 32 * lg;
+#pragma unroll
+      for (int q4 = 0; q4 < 8; ++q4) m.a[it][q4] = *reinterpret_cast<const float4 *>(arow + 4 * q4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) m.b[it][r] = A[(size_t)(row0 + 4 * lg + r) * (2 * D) + D + c0 + lr];
+    }
+  };
+  MapRows cur;
+  if (n_seg > 1) load_map(cur, 0);
+  __syncthreads();
+  for (int s = 0; s + 1 < n_seg; ++s) {
+    MapRows nxt;
+    if (s + 2 < n_seg) load_map(nxt, s + 1);
+    f32x4 res[2];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      f32x4 c[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
       for (int q4 = 0; q4 < 8; ++q4) {
-        const float4 av = *reinterpret_cast<const float4 *>(arow + 4 * q4);
+        const float4 av = cur.a[it][q4];
         const float4 bv = *reinterpret_cast<const float4 *>(&sXt[lr][32 * lg + 4 * q4]);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, c, 0, 0, 0);
-        c = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, c, 0, 0, 0);
+        c[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, c[0], 0, 0, 0);
+        c[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, c[1], 0, 0, 0);
+        c[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, c[2], 0, 0, 0);
+        c[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, c[3], 0, 0, 0);
       }
-      acc[it] = c;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) res[it][r] = ((c[0][r] + c[1][r]) + (c[2][r] + c[3][r])) + cur.b[it][r];
     }
     __syncthreads();   // all reads of the old block done
     float *dst = sin + ((size_t)bh * n_seg + s + 1) * D * D;
@@ -612,11 +655,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *__restr
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = (2 * wave + it) * 16 + 4 * lg + r;
-        const float v = acc[it][r] + A[(size_t)i * (2 * D) + D + c0 + lr];
-        sXt[lr][i] = v;
-        dst[(size_t)i * D + c0 + lr] = v;
+        sXt[lr][i] = res[it][r];
+        dst[(size_t)i * D + c0 + lr] = res[it][r];
       }
     __syncthreads();
+    if (s + 2 < n_seg) cur = nxt;
   }
 }
 
@@ -662,20 +705,24 @@ hipError_t launch_one(const StateArgs &a, hipStream_t s) {
   constexpr int VS = (MODE == MODE_TRANSITION ? 2 * D : D) / NC;
   const int groups = (a.n_units + 7) / 8;
   const unsigned grid = static_cast<unsigned>(groups) * 8u * VS;
-  hipLaunchKernelGGL((chunk_state_kernel<C, NC, F32, MODE, GATE>), dim3(grid), dim3(NC * 4), 0, s, a);
+  hipLaunchKernelGGL((chunk_state_kernel<C, NC, F32, MODE, GATE>), dim3(grid), dim3(Shape<NC, MODE>::NTH), 0, s, a);
   return hipGetLastError();
 }
 
 template <int C, bool F32, int MODE>
 hipError_t launch_nc(const StateArgs &a, int nc, hipStream_t s) {
-  if (nc == 128) {
-    if constexpr (MODE == MODE_OUTPUT) {
+  // a state map [A | B] (2D columns) is one workgroup of 8 waves x 32 columns
+  if constexpr (MODE == MODE_TRANSITION) {
+    (void)nc;
+    return launch_one<C, 2 * D, F32, MODE, false>(a, s);
+  } else {
+    if (nc == 128) {
       if (a.fused_gate) return launch_one<C, 128, F32, MODE, true>(a, s);
+      return launch_one<C, 128, F32, MODE, false>(a, s);
     }
-    return launch_one<C, 128, F32, MODE, false>(a, s);
+    if (nc == 64) return launch_one<C, 64, F32, MODE, false>(a, s);
+    return hipErrorInvalidValue;
   }
-  if (nc == 64) return launch_one<C, 64, F32, MODE, false>(a, s);
-  return hipErrorInvalidValue;
 }
 
 template <int MODE>
@@ -735,11 +782,10 @@ hipError_t launch_prefill(const kda_prefill_desc &d, const PrefillPlan &p, hipSt
     // pass 1: maps of all segments but the last
     StateArgs t = a;
     t.fused_gate = 0;
-    // the map [A | B] has 2 x 128 columns: two workgroups per segment
-    e = launch_mode<MODE_TRANSITION>(t, d.chunk, f32, D, s);
+    e = launch_mode<MODE_TRANSITION>(t, d.chunk, f32, 2 * D, s);
     if (e != hipSuccess) return e;
     // pass 2: states entering each segment
-    const unsigned grid = static_cast<unsigned>(units * (D / 16));
+    const unsigned grid = static_cast<unsigned>((units + 7) / 8 * 8 * (D / 16));
     hipLaunchKernelGGL(segment_scan, dim3(grid), dim3(NTHREADS), 0, s, maps, d.S0, sin, p.n_seg,
                        static_cast<int>(units));
     e = hipGetLastError();
