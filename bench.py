@@ -186,8 +186,9 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
-            "kernel": "one prefill call per step (prefill_kernel, plus norm_gate_kernel when "
-                      "the value columns of a head are split across workgroups)",
+            "kernel": "one prefill call per step: chunk_prep_kernel, chunk_state_kernel (state "
+                      "maps), segment_scan, chunk_state_kernel (outputs); their durations sum to "
+                      "the call",
             "alg_bytes_per_launch": alg_b,
             "kernel_ms_mean": round(kernel_ms, 4),
             "kernel_ms_median": round(durs[len(durs) // 2], 4),
