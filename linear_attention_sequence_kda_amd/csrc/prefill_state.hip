@@ -599,7 +599,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *__restr
                                                            const float *__restrict__ S0,
                                                            float *__restrict__ sin, int n_seg,
                                                            int n_bh) {
-  __shared__ __align__(16) float sXt[16][D + 4];      // current state block, transposed [n][i]
+  __shared__ __align__(16) float sXt[2][16][D + 4];   // state block, transposed [n][i], double buffered
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
@@ -610,7 +610,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *__restr
   for (int x = tid; x < 16 * D; x += NTHREADS) {
     const int i = x / 16, n = x % 16;
     const float v = S0 ? S0[(size_t)bh * D * D + (size_t)i * D + c0 + n] : 0.f;
-    sXt[n][i] = v;
+    sXt[0][n][i] = v;
     sin[((size_t)bh * n_seg) * D * D + (size_t)i * D + c0 + n] = v;
   }
   // wave w computes rows 32w .. 32w + 31 (two 16-row tiles)
@@ -639,7 +639,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *__restr
 #pragma unroll
       for (int q4 = 0; q4 < 8; ++q4) {
         const float4 av = cur.a[it][q4];
-        const float4 bv = *reinterpret_cast<const float4 *>(&sXt[lr][32 * lg + 4 * q4]);
+        const float4 bv = *reinterpret_cast<const float4 *>(&sXt[s & 1][lr][32 * lg + 4 * q4]);
         c[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, c[0], 0, 0, 0);
         c[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, c[1], 0, 0, 0);
         c[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, c[2], 0, 0, 0);
@@ -648,17 +648,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *__restr
 #pragma unroll
       for (int r = 0; r < 4; ++r) res[it][r] = ((c[0][r] + c[1][r]) + (c[2][r] + c[3][r])) + cur.b[it][r];
     }
-    __syncthreads();   // all reads of the old block done
     float *dst = sin + ((size_t)bh * n_seg + s + 1) * D * D;
 #pragma unroll
     for (int it = 0; it < 2; ++it)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = (2 * wave + it) * 16 + 4 * lg + r;
-        sXt[lr][i] = res[it][r];
+        sXt[(s + 1) & 1][lr][i] = res[it][r];   // the other buffer: no wait for readers of this one
         dst[(size_t)i * D + c0 + lr] = res[it][r];
       }
-    __syncthreads();
+    // the new block visible to all waves; a barrier without a memory fence, so that the
+    // global stores of the block are not waited for
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
     if (s + 2 < n_seg) cur = nxt;
   }
 }
