@@ -238,6 +238,57 @@ def main():
                          "alg_bytes_per_launch": db},
         }
 
+    # ---------------- serving: decode over a state pool, write-back to host ----------------
+    if not a.no_decode:
+        P, N, Hs, steps = 1024, 256, 16, 200
+        pool = torch.empty((P, Hs, D, D), dtype=torch.float32, device=dev)
+        for i in range(0, P, N):                                   # seeded states, 256 at a time
+            pool[i:i + N] = up(make_decode_state(N, Hs, D, seed=1 + i // N))
+        slots = torch.from_numpy(np.random.default_rng(1).permutation(P)[:N].astype(np.int32)).to(dev)
+        Xp = make_decode_steps(N, Hs, D, seed=1, steps=16)
+        XP = {kk: up(vv) for kk, vv in Xp.items()}
+        op = torch.empty((N, Hs, D), dtype=torch.float32, device=dev)
+
+        def pstep(s):
+            j = s % 16
+            kda.kda_decode_step_pooled(XP["q"][j], XP["k"][j], XP["v"][j], XP["g"][j], XP["beta"][j],
+                                       pool, slots, o=op, stream=stream)
+
+        for s in range(5):
+            pstep(s)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for s in range(steps):
+            pstep(s)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        db = decode_alg_bytes(N, Hs) + N * 4
+        # write-back of the active sequences' states to pinned host memory
+        host = torch.empty((N, Hs, D, D), dtype=torch.float32, pin_memory=True)
+        kda.kda_state_copy_indexed(host, pool, src_slots=slots, stream=stream)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(3):
+            kda.kda_state_copy_indexed(host, pool, src_slots=slots, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wb_ms = e0.elapsed_time(e1) / 3
+        out["decode_pooled"] = {
+            "workload": f"decode over a pool of {P} sequences x H={Hs} (fp32 states, 1 GiB), "
+                        f"{N} active sequences at seeded slots, {steps} steps",
+            "seq_steps_per_s": round(N / (us * 1e-6), 1),
+            "us_per_step": round(us, 2),
+            "roofline": {"bound": "hbm", "achieved": round(db / (us * 1e-6) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(db / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                         "alg_bytes_per_launch": db},
+            "write_back_to_pinned_host": {"bytes": N * Hs * D * D * 4, "ms": round(wb_ms, 3),
+                                          "GB_per_s": round(N * Hs * D * D * 4 / (wb_ms * 1e-3) / 1e9, 1)},
+        }
+        del pool, host
+
     # one copy kernel of known size (state checkpoint, 64 MiB each way) after the timed regions:
     # counter runs use it to calibrate FETCH_SIZE / WRITE_SIZE against known bytes
     cal_src = torch.zeros((1024, D, D), dtype=torch.float32, device=dev)

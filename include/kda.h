@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 #if defined(__GNUC__) || defined(__clang__)
 #define KDA_API __attribute__((visibility("default")))
@@ -118,7 +118,7 @@ typedef struct kda_prefill_desc {
   int32_t v_split;          /* 0 = choose (1); 1 or 2 workgroups per (seq, head)
                                splitting the d_v columns of the state */
   void *workspace;          /* device scratch of kda_prefill_workspace_size() bytes:
-                               per-chunk records (about 64.5 KB per chunk and head),
+                               per-chunk records (61 KiB per 64-token chunk and head),
                                plus segment maps and raw outputs when used */
   size_t workspace_bytes;
 } kda_prefill_desc;
@@ -160,6 +160,21 @@ typedef struct kda_decode_desc {
 KDA_API kda_status kda_decode_step(const kda_decode_desc *d, hipStream_t stream);
 
 /*
+ * Serving: one decode step for a batch whose states live in a pool of slots ([S]:
+ * the serving path keeps per-sequence states; this is kda_decode_step with an
+ * indirection).  d->state is the pool, [pool_size, H, d_k, d_v] fp32.  Sequence n of
+ * the batch (its rows of q, k, v, g, beta, gate and o, laid out [N, H, ...] as in
+ * kda_decode_desc) reads and updates, in place, the states of slot slots[n].
+ * slots: DEVICE array of N int32, distinct (two sequences on one slot race).  A slot
+ * outside [0, pool_size) is not visible to the host: that sequence's o row is NaN
+ * and the pool is not touched for it.  Slots no sequence names are not touched.
+ * Errors: as kda_decode_step, plus NULL (slots when N * H > 0), SHAPE
+ * (pool_size < 0), and ALIAS when the pool overlaps o or an input.
+ */
+KDA_API kda_status kda_decode_step_pooled(const kda_decode_desc *d, const int32_t *slots,
+                                          int32_t pool_size, hipStream_t stream);
+
+/*
  * State checkpoint and rollback ([S]: state rollback is one of KDA's execution
  * forms; the prefix cache keeps checkpoints).  Both copy n_states fp32 states of
  * d_k x d_v on the stream: checkpoint ckpt[i] = state[i], rollback
@@ -171,6 +186,27 @@ KDA_API kda_status kda_state_checkpoint(const float *state, float *ckpt, int64_t
                                 int32_t d_v, hipStream_t stream);
 KDA_API kda_status kda_state_rollback(float *state, const float *ckpt, int64_t n_states, int32_t d_k,
                               int32_t d_v, hipStream_t stream);
+
+/*
+ * Indexed state copy (serving: prefix-cache reuse from 512-token checkpoints, moving
+ * states in and out of a pool, write-back to host; [S]).  For i < n:
+ *     dst[dst_slots[i]] = src[src_slots[i]]
+ * where each element is one state of state_elems fp32 values (for instance
+ * H * d_k * d_v, all heads of a sequence; a prefill's checkpoints
+ * [B, T/ckpt_every, H, d_k, d_v] are B * T/ckpt_every such states).  A NULL slot
+ * array means slot i.  dst holds dst_count states and src holds src_count; a pair
+ * with a slot outside its array is skipped.  dst and src are device memory or
+ * pinned host memory the device can access (hipHostMalloc), so write-back to host
+ * is this call with a host dst.  Slot arrays are DEVICE arrays of n int32.  The
+ * copies run in parallel: destinations must be distinct and no destination may be a
+ * source of the same call.  Errors: NULL (dst or src when n > 0 and
+ * state_elems > 0), SHAPE (a negative size, n above a count whose slot array is
+ * NULL, or more than 2^31 workgroups), DEVICE, HIP.
+ */
+KDA_API kda_status kda_state_copy_indexed(float *dst, const int32_t *dst_slots, int64_t dst_count,
+                                          const float *src, const int32_t *src_slots,
+                                          int64_t src_count, int64_t n, int64_t state_elems,
+                                          hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 KDA_API const char *kda_status_string(kda_status s);

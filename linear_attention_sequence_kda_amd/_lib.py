@@ -72,6 +72,11 @@ def load(path: str = LIB_PATH):
         lib.kda_prefill_chunked.restype = C.c_int
         lib.kda_decode_step.argtypes = [C.POINTER(DecodeDesc), vp]
         lib.kda_decode_step.restype = C.c_int
+        lib.kda_decode_step_pooled.argtypes = [C.POINTER(DecodeDesc), vp, C.c_int32, vp]
+        lib.kda_decode_step_pooled.restype = C.c_int
+        lib.kda_state_copy_indexed.argtypes = [vp, vp, C.c_int64, vp, vp, C.c_int64, C.c_int64,
+                                               C.c_int64, vp]
+        lib.kda_state_copy_indexed.restype = C.c_int
         lib.kda_state_checkpoint.argtypes = [vp, vp, C.c_int64, C.c_int32, C.c_int32, vp]
         lib.kda_state_checkpoint.restype = C.c_int
         lib.kda_state_rollback.argtypes = [vp, vp, C.c_int64, C.c_int32, C.c_int32, vp]
@@ -103,6 +108,27 @@ def _ptr(t):
     if not t.is_contiguous():
         raise ValueError("tensor must be contiguous")
     return t.data_ptr() if t.numel() > 0 else None
+
+
+def _ptr_any(t):
+    """Device tensor, or pinned host tensor (device-accessible at the same address)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not (t.is_cuda or t.is_pinned()):
+        raise ValueError("tensor must be on the HIP device or in pinned host memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr() if t.numel() > 0 else None
+
+
+def _slots(t):
+    if t is None:
+        return None
+    if t.dtype != torch.int32:
+        raise ValueError("slot arrays must be int32")
+    return _ptr(t)
 
 
 def _dtype(t) -> int:
@@ -170,9 +196,7 @@ def kda_prefill_chunked(q, k, v, g, beta, *, o, S0=None, S_final=None, gate=None
     _check("kda_prefill_chunked", load().kda_prefill_chunked(C.byref(d), _stream(stream)))
 
 
-def kda_decode_step(q, k, v, g, beta, state, *, o, gate=None, norm_weight=None, norm_eps=1e-6,
-                    stream=None) -> None:
-    """One decode step for [N,H,*] inputs; `state` [N,H,128,128] float32 is updated in place."""
+def _decode_desc(q, k, v, g, beta, state, o, gate, norm_weight, norm_eps) -> DecodeDesc:
     N, H, dk = q.shape
     d = DecodeDesc()
     d.N, d.H, d.d_k, d.d_v = N, H, dk, v.shape[-1]
@@ -180,7 +204,47 @@ def kda_decode_step(q, k, v, g, beta, state, *, o, gate=None, norm_weight=None, 
     d.q, d.k, d.v, d.g, d.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
     d.state, d.o, d.gate = _ptr(state), _ptr(o), _ptr(gate)
     d.norm_weight, d.norm_eps = _ptr(norm_weight), float(norm_eps)
+    return d
+
+
+def kda_decode_step(q, k, v, g, beta, state, *, o, gate=None, norm_weight=None, norm_eps=1e-6,
+                    stream=None) -> None:
+    """One decode step for [N,H,*] inputs; `state` [N,H,128,128] float32 is updated in place."""
+    d = _decode_desc(q, k, v, g, beta, state, o, gate, norm_weight, norm_eps)
     _check("kda_decode_step", load().kda_decode_step(C.byref(d), _stream(stream)))
+
+
+def kda_decode_step_pooled(q, k, v, g, beta, pool, slots, *, o, gate=None, norm_weight=None,
+                           norm_eps=1e-6, stream=None) -> None:
+    """One decode step for [N,H,*] inputs whose states are pool[slots[n]]: `pool`
+    [P,H,128,128] float32 is updated in place; `slots` is an int32 device tensor [N]."""
+    if slots is not None and slots.numel() != q.shape[0]:
+        raise ValueError("slots must hold one slot per sequence")
+    d = _decode_desc(q, k, v, g, beta, pool, o, gate, norm_weight, norm_eps)
+    _check("kda_decode_step_pooled",
+           load().kda_decode_step_pooled(C.byref(d), _slots(slots), int(pool.shape[0]),
+                                         _stream(stream)))
+
+
+def kda_state_copy_indexed(dst, src, *, dst_slots=None, src_slots=None, n=None,
+                           stream=None) -> None:
+    """dst[dst_slots[i]] = src[src_slots[i]] for i < n (slot i where a slot tensor is None).
+
+    dst, src: float32 [count, ...] with equal trailing shapes (one state per leading
+    index), on the device or in pinned host memory; slot tensors: int32 on the device."""
+    if dst.dtype != torch.float32 or src.dtype != torch.float32:
+        raise ValueError("states are float32")
+    if dst.shape[1:] != src.shape[1:]:
+        raise ValueError("dst and src states differ in shape")
+    if n is None:
+        n = (dst_slots if dst_slots is not None else src_slots if src_slots is not None else dst).shape[0]
+    elems = 1
+    for x in dst.shape[1:]:
+        elems *= int(x)
+    _check("kda_state_copy_indexed",
+           load().kda_state_copy_indexed(_ptr_any(dst), _slots(dst_slots), int(dst.shape[0]),
+                                         _ptr_any(src), _slots(src_slots), int(src.shape[0]),
+                                         int(n), elems, _stream(stream)))
 
 
 def _n_states(t) -> int:

@@ -153,9 +153,10 @@ kda_status validate_prefill(const kda_prefill_desc *d, PrefillPlan *p) {
   return KDA_OK;
 }
 
-kda_status validate_decode(const kda_decode_desc *d) {
+// n_state: states in d->state (N for the plain form, the pool size for the pooled one)
+kda_status validate_decode(const kda_decode_desc *d, int64_t n_state) {
   if (!d) return KDA_ERR_NULL;
-  if (d->N < 0 || d->H < 0) return KDA_ERR_SHAPE;
+  if (d->N < 0 || d->H < 0 || n_state < 0) return KDA_ERR_SHAPE;
   if (d->d_k != 128 || d->d_v != 128) return KDA_ERR_UNSUPPORTED;
   if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return KDA_ERR_UNSUPPORTED;
   const size_t n = static_cast<size_t>(d->N) * d->H;
@@ -163,7 +164,8 @@ kda_status validate_decode(const kda_decode_desc *d) {
   if (!d->q || !d->k || !d->v || !d->g || !d->beta || !d->state || !d->o) return KDA_ERR_NULL;
   const size_t ie = esize(d->in_dtype), oe = esize(d->out_dtype);
   const size_t dk = d->d_k, dv = d->d_v;
-  const size_t o_bytes = n * dv * oe, s_bytes = n * dk * dv * 4;
+  const size_t o_bytes = n * dv * oe;
+  const size_t s_bytes = static_cast<size_t>(n_state) * d->H * dk * dv * 4;
   struct R { const void *p; size_t n; } in[] = {
       {d->q, n * dk * ie}, {d->k, n * dk * ie}, {d->v, n * dv * ie}, {d->g, n * dk * 4},
       {d->beta, n * 4},    {d->gate, d->gate ? n * dv * ie : 0},
@@ -181,6 +183,18 @@ kda_status validate_copy(const float *a, const float *b, int64_t n_states, int32
   if (!a || !b) return KDA_ERR_NULL;
   const size_t bytes = static_cast<size_t>(n_states) * dk * dv * 4;
   if (overlap(a, bytes, b, bytes)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+kda_status validate_copy_indexed(const float *dst, int64_t dst_count, const int32_t *dst_slots,
+                                 const float *src, int64_t src_count, const int32_t *src_slots,
+                                 int64_t n, int64_t elems) {
+  if (n < 0 || dst_count < 0 || src_count < 0 || elems < 0) return KDA_ERR_SHAPE;
+  if ((!dst_slots && n > dst_count) || (!src_slots && n > src_count)) return KDA_ERR_SHAPE;
+  if (n == 0 || elems == 0) return KDA_OK;
+  if (!dst || !src) return KDA_ERR_NULL;
+  const int64_t pieces = (elems + 1023) / 1024;            // workgroups per state (grid size)
+  if (pieces > (int64_t(1) << 31) / n) return KDA_ERR_SHAPE;
   return KDA_OK;
 }
 
@@ -212,12 +226,34 @@ kda_status kda_prefill_chunked(const kda_prefill_desc *d, hipStream_t stream) {
 }
 
 kda_status kda_decode_step(const kda_decode_desc *d, hipStream_t stream) {
-  kda_status st = validate_decode(d);
+  kda_status st = validate_decode(d, d ? d->N : 0);
   if (st != KDA_OK) return st;
   if (static_cast<int64_t>(d->N) * d->H == 0) return KDA_OK;
   st = check_device();
   if (st != KDA_OK) return st;
-  return from_hip(kda::launch_decode(*d, stream));
+  return from_hip(kda::launch_decode(*d, nullptr, 0, stream));
+}
+
+kda_status kda_decode_step_pooled(const kda_decode_desc *d, const int32_t *slots, int32_t pool_size,
+                                  hipStream_t stream) {
+  kda_status st = validate_decode(d, pool_size);
+  if (st != KDA_OK) return st;
+  if (static_cast<int64_t>(d->N) * d->H == 0) return KDA_OK;
+  if (!slots) return KDA_ERR_NULL;
+  st = check_device();
+  if (st != KDA_OK) return st;
+  return from_hip(kda::launch_decode(*d, slots, pool_size, stream));
+}
+
+kda_status kda_state_copy_indexed(float *dst, const int32_t *dst_slots, int64_t dst_count,
+                                  const float *src, const int32_t *src_slots, int64_t src_count,
+                                  int64_t n, int64_t state_elems, hipStream_t stream) {
+  kda_status st = validate_copy_indexed(dst, dst_count, dst_slots, src, src_count, src_slots, n, state_elems);
+  if (st != KDA_OK || n == 0 || state_elems == 0) return st;
+  st = check_device();
+  if (st != KDA_OK) return st;
+  return from_hip(kda::launch_state_copy_indexed(dst, dst_slots, dst_count, src, src_slots, src_count, n,
+                                                  state_elems, stream));
 }
 
 kda_status kda_state_checkpoint(const float *state, float *ckpt, int64_t n_states, int32_t d_k,

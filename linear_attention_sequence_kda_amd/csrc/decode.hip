@@ -11,6 +11,10 @@
 //
 // Thread layout (256 threads): column group cg = tid % 32 owns columns 4cg..4cg+3;
 // row phase rp = tid / 32 owns rows rp, rp+8, ..., rp+120 (16 rows).
+//
+// Pooled form (serving): the states live in a pool of slots and sequence n of the
+// batch uses slot slots[n]; everything else is as above.  A slot outside the pool
+// leaves the pool untouched and gives NaN outputs for that sequence.
 #include "internal.h"
 #include "kda_device.h"
 
@@ -27,6 +31,8 @@ struct DecodeArgs {
   float *state;
   void *o;
   float eps;
+  const int32_t *slots;   // pooled form: slot of each sequence, or null
+  int32_t pool, H;        // pool size (slots), heads
 };
 
 template <bool IN_BF16, bool OUT_BF16, bool GATE>
@@ -38,7 +44,17 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int cg = tid & 31, rp = tid >> 5, wave = tid >> 6, lane = tid & 63;
   const size_t nh = blockIdx.x;                       // sequence * H + head
-  float *S = a.state + nh * (size_t)(D * D);
+  size_t sh = nh;                                      // state index in the pool
+  if (a.slots) {
+    const int n = (int)(nh / a.H), h = (int)(nh % a.H);
+    const int slot = a.slots[n];
+    if (slot < 0 || slot >= a.pool) {                  // not a slot of the pool
+      if (tid < D / 4) store4<OUT_BF16>(a.o, nh * D + 4 * tid, make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")));
+      return;
+    }
+    sh = (size_t)slot * a.H + h;
+  }
+  float *S = a.state + sh * (size_t)(D * D);
 
   // Issue the 16 state loads first so their latency overlaps the small vector loads.
   float4 s[ROWS_PER_T];
@@ -121,10 +137,11 @@ hipError_t launch3(const DecodeArgs &a, unsigned n_blocks, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_decode(const kda_decode_desc &d, hipStream_t s) {
+hipError_t launch_decode(const kda_decode_desc &d, const int32_t *slots, int32_t pool, hipStream_t s) {
   const int64_t n = (int64_t)d.N * d.H;
   if (n == 0) return hipSuccess;
-  DecodeArgs a{d.q, d.k, d.v, d.gate, d.g, d.beta, d.norm_weight, d.state, d.o, d.norm_eps};
+  DecodeArgs a{d.q, d.k, d.v, d.gate, d.g, d.beta, d.norm_weight, d.state, d.o, d.norm_eps,
+               slots, pool, d.H};
   const bool ib = d.in_dtype == KDA_BF16, ob = d.out_dtype == KDA_BF16, gt = d.gate != nullptr;
   const unsigned nb = static_cast<unsigned>(n);
   if (ib) {

@@ -9,7 +9,14 @@
 
 namespace kda {
 
-hipError_t launch_decode(const kda_decode_desc &d, hipStream_t s);
+// slots: null for the plain form (state [N, H, d_k, d_v]); else the pool slot of each
+// sequence (state [pool, H, d_k, d_v]).
+hipError_t launch_decode(const kda_decode_desc &d, const int32_t *slots, int32_t pool, hipStream_t s);
+// dst[dst_slots[i]] = src[src_slots[i]] for i < n (identity where a slot array is null),
+// states of `elems` floats; pairs with a slot outside [0, count) are skipped.
+hipError_t launch_state_copy_indexed(float *dst, const int32_t *dst_slots, int64_t dst_count,
+                                     const float *src, const int32_t *src_slots, int64_t src_count,
+                                     int64_t n, int64_t elems, hipStream_t s);
 hipError_t launch_state_copy(float *dst, const float *src, int64_t n_floats, hipStream_t s);
 hipError_t launch_fill_zero(float *dst, int64_t n_floats, hipStream_t s);
 

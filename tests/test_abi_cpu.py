@@ -21,9 +21,9 @@ def _declared():
 
 def test_header_declares_entry_points():
     names = _declared()
-    for n in ("kda_prefill_chunked", "kda_decode_step", "kda_state_checkpoint",
-              "kda_state_rollback", "kda_prefill_workspace_size", "kda_status_string",
-              "kda_abi_version"):
+    for n in ("kda_prefill_chunked", "kda_decode_step", "kda_decode_step_pooled",
+              "kda_state_checkpoint", "kda_state_rollback", "kda_state_copy_indexed",
+              "kda_prefill_workspace_size", "kda_status_string", "kda_abi_version"):
         assert n in names
 
 
@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.kda_abi_version() == 1
+    assert kda.kda_abi_version() == 2
     seen = set()
     for st in range(8):
         s = kda.status_string(st)
@@ -153,3 +153,31 @@ def test_copy_validation_errors():
     assert lib.kda_state_rollback(None, FAKE, 1, 128, 128, None) == kda.KDA_ERR_NULL
     assert lib.kda_state_rollback(FAKE, FAKE + (1 << 20), -1, 128, 128, None) == kda.KDA_ERR_SHAPE
     assert lib.kda_state_checkpoint(FAKE, FAKE + (1 << 20), 0, 128, 128, None) == kda.KDA_OK
+
+
+def test_pooled_decode_validation_errors():
+    lib = _lib.load()
+    f = lambda d, slots, pool: lib.kda_decode_step_pooled(C.byref(d), slots, pool, None)  # noqa: E731
+    assert lib.kda_decode_step_pooled(None, FAKE, 4, None) == kda.KDA_ERR_NULL
+    assert f(_ddesc(), None, 8) == kda.KDA_ERR_NULL                   # slots missing
+    assert f(_ddesc(), FAKE + (1 << 33), -1) == kda.KDA_ERR_SHAPE      # negative pool
+    assert f(_ddesc(d_k=64), FAKE + (1 << 33), 8) == kda.KDA_ERR_UNSUPPORTED
+    d = _ddesc()
+    d.state = d.g - 4096                                             # an 8-slot pool over g
+    assert f(d, FAKE + (1 << 33), 8) == kda.KDA_ERR_ALIAS
+    assert f(_ddesc(N=0), None, 8) == kda.KDA_OK                       # empty batch: no-op
+
+
+def test_indexed_copy_validation_errors():
+    lib = _lib.load()
+    f = lib.kda_state_copy_indexed
+    S = 16 * 128 * 128
+    assert f(None, None, 4, FAKE, None, 4, 4, S, None) == kda.KDA_ERR_NULL
+    assert f(FAKE, None, 4, None, None, 4, 4, S, None) == kda.KDA_ERR_NULL
+    assert f(FAKE, None, 4, FAKE + (1 << 34), None, 4, -1, S, None) == kda.KDA_ERR_SHAPE
+    assert f(FAKE, None, 4, FAKE + (1 << 34), None, 4, 4, -5, None) == kda.KDA_ERR_SHAPE
+    assert f(FAKE, None, 2, FAKE + (1 << 34), None, 4, 3, S, None) == kda.KDA_ERR_SHAPE  # n > dst_count
+    assert f(FAKE, None, 4, FAKE + (1 << 34), None, 2, 3, S, None) == kda.KDA_ERR_SHAPE  # n > src_count
+    # with slot arrays, counts only bound the slots (checked on the device)
+    assert f(None, FAKE, 2, None, FAKE, 2, 0, S, None) == kda.KDA_OK   # nothing to copy
+    assert f(FAKE, FAKE + 64, 1, FAKE + (1 << 34), None, 1 << 40, 1 << 30, 1 << 20, None) == kda.KDA_ERR_SHAPE
