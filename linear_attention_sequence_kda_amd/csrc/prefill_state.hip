@@ -189,6 +189,7 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
   constexpr int CBW = NCW / 16;                        // 16-column blocks per wave
   constexpr int VC = SH::VC;                           // value columns in LDS
   static_assert(!GATE || (MODE == MODE_OUTPUT && NC == D), "the fused epilogue needs whole heads");
+  static_assert(MODE == MODE_OUTPUT || (NC == 2 * D && CBW == 2), "a state map is one workgroup, two blocks per wave");
   constexpr int VS = (MODE == MODE_TRANSITION ? 2 * D : D) / NC;   // workgroups per unit
   // KiB of the record this pass copies (the state map needs only its prefix)
   constexpr int NBLK = (int)((MODE == MODE_TRANSITION ? R::trans : R::bytes) / 1024);
@@ -221,6 +222,12 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
   const int h = bh % a.H, b = bh / a.H;
   const int c0 = slice * NC;                           // first (virtual) column of this slice
   const int cw = wave * NCW;                           // this wave's first column in the slice
+  // First column of 16-column block j of this wave.  A state map gives each wave one
+  // block of the A part and the matching block of the B part, so that every wave has
+  // the same work (only B blocks carry values).
+  auto colb = [&](int j) __attribute__((always_inline)) {
+    return MODE == MODE_TRANSITION ? j * D + 16 * wave : c0 + cw + 16 * j;
+  };
   const size_t tok_stride = (size_t)a.H * D;
   const size_t state_off = (size_t)bh * D * D;
   const unsigned char *rec_bh = a.rec + (size_t)bh * a.n_chunks * R::bytes;
@@ -233,13 +240,13 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
     for (int x = tid; x < (KC - C) * VC; x += NTH) sVA[C * VC + x] = sVB[C * VC + x] = T(0);
   }
 
-  // ---- initial state: S[ib][j] holds rows 16ib + 4lg + r, column c0 + cw + 16j + lr
+  // ---- initial state: S[ib][j] holds rows 16ib + 4lg + r, column colb(j) + lr
   f32x4 S[8][CBW];
 #pragma unroll
   for (int ib = 0; ib < 8; ++ib)
 #pragma unroll
     for (int j = 0; j < CBW; ++j) {
-      const int c = c0 + cw + 16 * j + lr;
+      const int c = colb(j) + lr;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = 16 * ib + 4 * lg + r;
@@ -427,14 +434,14 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < CBW; ++j) sf[kb][j] = frag_from<F32>(S[2 * kb][j], S[2 * kb + 1][j]);
-    // the A part of a state map (columns < D) carries no values: no T V product there
-    const bool has_v = MODE == MODE_OUTPUT || c0 + cw >= D;        // wave-uniform
-    if (has_v) {
+    // the A part of a state map (block 0 of each wave) carries no values: no T V product
+    // there
+    auto has_v = [&](int j) __attribute__((always_inline)) { return MODE == MODE_OUTPUT || j == 1; };
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int j = 0; j < CBW; ++j) vf[kb][j] = ld_t_split<F32, VC>(sV, 32 * kb, cw - SH::VOFF + 16 * j, lane);
-    }
+      for (int j = 0; j < CBW; ++j)
+        if (has_v(j)) vf[kb][j] = ld_t_split<F32, VC>(sV, 32 * kb, colb(j) - SH::VOFF - c0, lane);
 
     // The products run as independent accumulation chains, one per output tile, stepped
     // together over the contraction blocks, so that consecutive MFMAs do not wait on
@@ -461,10 +468,9 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
       for (int tb = 0; tb < NT; ++tb) {
         if (!R::nz(tb, kb)) continue;                  // T is lower triangular
         const V8 tf = take(fi++);
-        if (has_v) {
 #pragma unroll
-          for (int j = 0; j < CBW; ++j) U[tb][j] = Op<F32>::mma(U[tb][j], tf, vf[kb][j]);
-        }
+        for (int j = 0; j < CBW; ++j)
+          if (has_v(j)) U[tb][j] = Op<F32>::mma(U[tb][j], tf, vf[kb][j]);
       }
     // U as an operand (contraction over tokens; tokens past the chunk are zero)
     V8 uf[KB][CBW];
@@ -573,7 +579,7 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
       for (int j = 0; j < CBW; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          dst[(size_t)(16 * ib + 4 * lg + r) * (2 * D) + c0 + cw + 16 * j + lr] = S[ib][j][r];
+          dst[(size_t)(16 * ib + 4 * lg + r) * (2 * D) + colb(j) + lr] = S[ib][j][r];
   }
   // the copies of the last iteration (a reload of the last chunk) complete before the
   // workgroup's LDS is released
