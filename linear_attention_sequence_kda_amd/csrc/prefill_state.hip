@@ -601,10 +601,10 @@ struct MapRows {
   float b[2][4];      // B at rows 4lg + r of each tile, this lane's column
 };
 
-__global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *__restrict__ maps,
-                                                           const float *__restrict__ S0,
-                                                           float *__restrict__ sin, int n_seg,
-                                                           int n_bh) {
+// (no __restrict__ on the maps: with it the compiler sinks the prefetch loads of the
+// next map to their uses, exposing their latency at every step)
+__global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *maps, const float *S0, float *sin,
+                                                           int n_seg, int n_bh) {
   __shared__ __align__(16) float sXt[2][16][D + 4];   // state block, transposed [n][i], double buffered
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
@@ -632,12 +632,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *__restr
       for (int r = 0; r < 4; ++r) m.b[it][r] = A[(size_t)(row0 + 4 * lg + r) * (2 * D) + D + c0 + lr];
     }
   };
-  MapRows cur;
-  if (n_seg > 1) load_map(cur, 0);
+  // Two map buffers in fixed roles per half of the unrolled loop (no register copies
+  // between them), so that the waits for one map's rows do not cover the loads of the
+  // next one.
+  MapRows m0, m1;
+  if (n_seg > 1) load_map(m0, 0);
   __syncthreads();
-  for (int s = 0; s + 1 < n_seg; ++s) {
-    MapRows nxt;
-    if (s + 2 < n_seg) load_map(nxt, s + 1);
+  auto step = [&](MapRows &cur, MapRows &nxt, int s) __attribute__((always_inline)) {
+    // unconditional (the last step reloads the last map), so that the compiler's waits
+    // for cur count exactly the loads issued after it
+    load_map(nxt, min(s + 1, n_seg - 2));
     f32x4 res[2];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -669,7 +673,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *__restr
     __builtin_amdgcn_s_waitcnt(0xC07F);                // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (s + 2 < n_seg) cur = nxt;
+  };
+  for (int s = 0; s + 1 < n_seg; s += 2) {
+    step(m0, m1, s);
+    if (s + 2 < n_seg) step(m1, m0, s + 1);
   }
 }
 
