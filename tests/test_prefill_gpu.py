@@ -159,6 +159,21 @@ def test_segments(n_seg):
     check(c, f"segments={n_seg}", chunk=64, n_segments=n_seg, ckpt_every=256)
 
 
+@pytest.mark.parametrize("v_split,out_dtype", [(1, torch.float32), (2, torch.float32),
+                                               (2, torch.bfloat16)])
+def test_segments_with_gate(v_split, out_dtype):
+    """Segments, the fused or separate norm/gate pass, fp32 or bf16 outputs, ragged tail."""
+    c = make_prefill(2, 900, 3, 128, seed=54, in_dtype=BF16, s0_std=0.05, gate=True)
+    w = np.random.default_rng(54).uniform(0.5, 1.5, 128).astype(np.float32)
+    check(c, f"segments gate v_split={v_split} {out_dtype}", chunk=64, n_segments=3,
+          v_split=v_split, gate=True, norm_weight=w, out_dtype=out_dtype)
+
+
+def test_segments_chunk16_gate():
+    c = make_prefill(1, 700, 2, 128, seed=55, in_dtype=BF16, s0_std=0.05, gate=True)
+    check(c, "segments chunk16 gate", chunk=16, n_segments=4, gate=True, ckpt_every=128)
+
+
 def test_segments_slow_decay():
     c = make_prefill(1, 2048, 2, 128, seed=52, in_dtype=BF16, pinned_floor_frac=0.1,
                      slow_frac=0.1)
