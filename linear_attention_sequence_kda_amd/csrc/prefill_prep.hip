@@ -57,11 +57,13 @@ struct PrepLayout {
   static constexpr size_t bVec = (size_t)(3 * NT + NFAC) * D * 4;   // per-tile decay vectors
   static constexpr size_t bAo = NBO > 0 ? (size_t)NBO * 256 * 2 : 0;   // A, off-diagonal blocks, fp16
   static constexpr size_t bX = (size_t)NT * 256 * E;  // inverses of the diagonal blocks of I + A
-  static constexpr size_t oKT = 0;
-  static constexpr size_t oKF = al(oKT + bKT);
+  // K e^G is written only after KF is dead (from the raw k still in registers), so it
+  // shares KF's storage
+  static constexpr size_t oKF = 0;
+  static constexpr size_t oKT = oKF;
   // T^T is written only after the diagonal A blocks and the per-tile vectors are dead,
   // so it shares their storage
-  static constexpr size_t oTt = al(oKF + bKF);
+  static constexpr size_t oTt = al(oKF + (bKF > bKT ? bKF : bKT));
   static constexpr size_t oAd = oTt;
   static constexpr size_t oDpow = oAd + bAd;                    // D_m = e^{tile m total}
   static constexpr size_t oPre = oDpow + (size_t)NT * D * 4;    // prod_{m<w} D_m
@@ -147,7 +149,9 @@ __device__ __forceinline__ void invert_unit_lower(const float *rowA, float *x, i
 }
 
 template <int C, bool F32>
-__global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepArgs a) {
+// 34 KB of LDS and at most 128 VGPRs at C = 64: four workgroups share a CU, and one's
+// loads overlap the others' arithmetic
+__global__ __launch_bounds__(NTHREADS, F32 ? 1 : (C == 64 ? 4 : 2)) void chunk_prep_kernel(PrepArgs a) {
   using L = PrepLayout<C, F32>;
   using R = Rec<C, F32>;
   using T = typename Op<F32>::T;
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
                 *reinterpret_cast<const float4 *>(sPre + wave * D + ch + 16));
         f8_from(dw, *reinterpret_cast<const float4 *>(sDpow + wave * D + ch),
                 *reinterpret_cast<const float4 *>(sDpow + wave * D + ch + 16));
-        float rk[8], rq[8], yd[8], xk[8], xf[8];
+        float rk[8], rq[8], yd[8], xf[8];
         V8 xq;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -275,14 +279,11 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
           yd[e] = kk * En;                             // k e^{r_w - G_t}
           xf[e] = yd[e] * dw[e];                       // k e^{r_{w+1} - G_t}, in [e^-75, 1] |k|
           xq[e] = Op<F32>::cvt(rq[e] * pre[e]);        // q e^{G_t}
-          xk[e] = rk[e] * pre[e];                      // k e^{G_t}
           rkx[kb][e] = Op<F32>::cvt(rk[e]);            // kept for the off-diagonal tiles
           rqx[kb][e] = Op<F32>::cvt(rq[e]);
         }
         // Qt goes out directly: this lane layout is the operand fragment (tile w, kb)
         Op<F32>::store(reinterpret_cast<T *>(out + R::frag(R::oQ, wave * 4 + kb, lane)), xq);
-        st4<F32, D>(sKT, tt, ch, xk[0], xk[1], xk[2], xk[3]);
-        st4<F32, D>(sKT, tt, ch + 16, xk[4], xk[5], xk[6], xk[7]);
         st4<F32, D>(sKF, tt, ch, xf[0], xf[1], xf[2], xf[3]);
         st4<F32, D>(sKF, tt, ch + 16, xf[4], xf[5], xf[6], xf[7]);
         // diagonal tile (w, w) straight from registers: A in bf16, P with bf16 hi/lo
@@ -404,6 +405,22 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
       Op<F32>::store(reinterpret_cast<T *>(out + R::frag(R::oK, f, lane)), v);
     }
     __syncthreads();   // A, P, diagonal inverses complete; KF dead
+    // K e^G = (k e^{G_t - r_w}) prod_{m<w} D_m into KF's storage, for W
+    if (wave < NT) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int ch = 32 * kb + 4 * lg;
+        float pre[8];
+        f8_from(pre, *reinterpret_cast<const float4 *>(sPre + wave * D + ch),
+                *reinterpret_cast<const float4 *>(sPre + wave * D + ch + 16));
+        float xk[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) xk[e] = static_cast<float>(rkx[kb][e]) * pre[e];
+        st4<F32, D>(sKT, tt, ch, xk[0], xk[1], xk[2], xk[3]);
+        st4<F32, D>(sKT, tt, ch + 16, xk[4], xk[5], xk[6], xk[7]);
+      }
+    }
+    __syncthreads();   // K e^G complete; the per-tile vectors are dead
 
     // ===== solve: wave w walks down column block w of X = (I + A)^-1:
     // X_{s,w} = -X_ss sum_{w<=m<s} A_{s,m} X_{m,w}; a 16x16 result in MFMA output layout
@@ -489,6 +506,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : 2) void chunk_prep_kernel(PrepA
 template <int C, bool F32>
 hipError_t launch_prep_t(const PrepArgs &a, hipStream_t s) {
   using L = PrepLayout<C, F32>;
+  static_assert(F32 || C != 64 || L::bytes <= 40 * 1024, "four workgroups per CU must fit in LDS");
   static_assert(L::bytes <= 53 * 1024, "three workgroups per CU must fit in LDS");
   auto kern = chunk_prep_kernel<C, F32>;
   static std::atomic<bool> attr_set{false};   // the attribute is per function, set once
