@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 #if defined(__GNUC__) || defined(__clang__)
 #define KDA_API __attribute__((visibility("default")))
@@ -207,6 +207,50 @@ KDA_API kda_status kda_state_copy_indexed(float *dst, const int32_t *dst_slots, 
                                           const float *src, const int32_t *src_slots,
                                           int64_t src_count, int64_t n, int64_t state_elems,
                                           hipStream_t stream);
+
+/*
+ * Gradients of the chunkwise prefill (training: [C] says the chunkwise form serves
+ * training as well as prefill).  Given dO = dL/do for the raw outputs o = S^T q of
+ * every token (before any norm or gate) and dS_final = dL/dS_T for the final state,
+ * computes dL/dq, dL/dk, dL/dv, dL/dg, dL/dbeta and dL/dS0 of the recurrence above.
+ * The gradient of g is zero where the clamp to [-5, 0] is active (g < -5 or g > 0)
+ * and passes at the two bounds.  fp32 arithmetic throughout (fp32 MFMA); every
+ * gradient is fp32.
+ */
+typedef struct kda_backward_desc {
+  int32_t B, T, H;          /* T >= 0; any T (a ragged last chunk is handled) */
+  int32_t d_k, d_v;         /* must be 128 */
+  int32_t chunk;            /* must be 64 */
+  int32_t in_dtype;         /* kda_dtype of q, k, v (as given to the prefill) */
+  const void *q;            /* [B,T,H,d_k] */
+  const void *k;            /* [B,T,H,d_k] */
+  const void *v;            /* [B,T,H,d_v] */
+  const float *g;           /* [B,T,H,d_k] log-decay as given to the prefill */
+  const float *beta;        /* [B,T,H] */
+  const float *S0;          /* [B,H,d_k,d_v] initial state, or NULL for zeros */
+  const float *dO;          /* [B,T,H,d_v] fp32 gradient of the raw outputs */
+  const float *dS_final;    /* [B,H,d_k,d_v] gradient of the final state, or NULL (zeros) */
+  float *dq, *dk;           /* [B,T,H,d_k] */
+  float *dv;                /* [B,T,H,d_v] */
+  float *dg;                /* [B,T,H,d_k] */
+  float *dbeta;             /* [B,T,H] */
+  float *dS0;               /* [B,H,d_k,d_v], or NULL when not wanted */
+  void *workspace;          /* device scratch of kda_backward_workspace_size() bytes:
+                               336.5 KiB per 64-token chunk and head (chunk
+                               quantities, and the state and its gradient at every
+                               chunk boundary) */
+  size_t workspace_bytes;
+} kda_backward_desc;
+
+/* Bytes of workspace kda_prefill_backward needs (pointers are not read).  Returns the
+ * same size errors as kda_prefill_backward. */
+KDA_API kda_status kda_backward_workspace_size(const kda_backward_desc *d, size_t *bytes);
+
+/* Enqueue the backward pass.  Errors: NULL (an input, dO or a gradient output when
+ * B*T*H > 0; workspace), SHAPE (negative sizes), UNSUPPORTED (d != 128, chunk != 64,
+ * bad dtype), WORKSPACE, ALIAS (a gradient output overlapping an input, another
+ * output or the workspace), DEVICE, HIP. */
+KDA_API kda_status kda_prefill_backward(const kda_backward_desc *d, hipStream_t stream);
 
 /* Static, NUL-terminated description of a status code. */
 KDA_API const char *kda_status_string(kda_status s);

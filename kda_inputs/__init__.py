@@ -31,14 +31,14 @@ import numpy as np
 __all__ = [
     "F32", "BF16", "f32_to_bf16", "bf16_to_f32", "to_f64",
     "PrefillCase", "DecodeStep", "WORKLOADS", "make_prefill", "make_workload", "make_decode_state",
-    "make_decode_step", "make_decode_steps", "workload",
+    "make_decode_step", "make_decode_steps", "workload", "make_output_grads",
 ]
 
 F32 = "f32"
 BF16 = "bf16"
 
 # Tensor ids for the per-tensor random streams.
-_Q, _K, _V, _G, _BETA, _GATE, _S0, _CHSEL = range(8)
+_Q, _K, _V, _G, _BETA, _GATE, _S0, _CHSEL, _DO, _DS = range(10)
 _BLOCK = 1024  # tokens per random stream block
 
 
@@ -328,3 +328,17 @@ def make_decode_steps(N: int, H: int, d: int = 128, *, seed: int = 0, steps: int
         for s in range(steps):
             work(s)
     return out
+
+
+def make_output_grads(B: int, T: int, H: int, d: int = 128, *, seed: int = 0,
+                      ds_std: float = 0.1) -> tuple[np.ndarray, np.ndarray]:
+    """Upstream gradients for the backward pass: dO ~ N(0, 1) as float32 [B,T,H,d]
+    (gradient of the raw outputs) and dS_T ~ N(0, ds_std) as float32 [B,H,d,d]
+    (gradient of the final state)."""
+    dO = np.empty((B, T, H, d), dtype=np.float32)
+    for b in range(B):
+        for blk in range((T + _BLOCK - 1) // _BLOCK):
+            t0, t1 = blk * _BLOCK, min(T, (blk + 1) * _BLOCK)
+            dO[b, t0:t1] = _normal(seed, _DO, b, blk, (t1 - t0, H, d)).astype(np.float32)
+    dS = _normal(seed, _DS, 0, 0, (B, H, d, d), scale=ds_std).astype(np.float32)
+    return dO, dS

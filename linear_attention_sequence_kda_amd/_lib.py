@@ -54,6 +54,19 @@ class DecodeDesc(C.Structure):
     ]
 
 
+class BackwardDesc(C.Structure):
+    _fields_ = [
+        ("B", C.c_int32), ("T", C.c_int32), ("H", C.c_int32),
+        ("d_k", C.c_int32), ("d_v", C.c_int32), ("chunk", C.c_int32), ("in_dtype", C.c_int32),
+        ("q", C.c_void_p), ("k", C.c_void_p), ("v", C.c_void_p),
+        ("g", C.c_void_p), ("beta", C.c_void_p), ("S0", C.c_void_p),
+        ("dO", C.c_void_p), ("dS_final", C.c_void_p),
+        ("dq", C.c_void_p), ("dk", C.c_void_p), ("dv", C.c_void_p), ("dg", C.c_void_p),
+        ("dbeta", C.c_void_p), ("dS0", C.c_void_p),
+        ("workspace", C.c_void_p), ("workspace_bytes", C.c_size_t),
+    ]
+
+
 _lib = None
 
 
@@ -81,6 +94,10 @@ def load(path: str = LIB_PATH):
         lib.kda_state_checkpoint.restype = C.c_int
         lib.kda_state_rollback.argtypes = [vp, vp, C.c_int64, C.c_int32, C.c_int32, vp]
         lib.kda_state_rollback.restype = C.c_int
+        lib.kda_backward_workspace_size.argtypes = [C.POINTER(BackwardDesc), C.POINTER(C.c_size_t)]
+        lib.kda_backward_workspace_size.restype = C.c_int
+        lib.kda_prefill_backward.argtypes = [C.POINTER(BackwardDesc), vp]
+        lib.kda_prefill_backward.restype = C.c_int
         lib.kda_status_string.argtypes = [C.c_int]
         lib.kda_status_string.restype = C.c_char_p
         lib.kda_abi_version.argtypes = []
@@ -267,3 +284,44 @@ def kda_state_rollback(state, ckpt, *, stream=None) -> None:
     _check("kda_state_rollback",
            load().kda_state_rollback(_ptr(state), _ptr(ckpt), _n_states(state), state.shape[-2],
                                      state.shape[-1], _stream(stream)))
+
+
+def _backward_desc(q, k, v, g, beta, dO, *, dq=None, dk=None, dv=None, dg=None, dbeta=None,
+                   S0=None, dS_final=None, dS0=None, chunk=64, workspace=None) -> BackwardDesc:
+    B, T, H, dk_ = q.shape
+    d = BackwardDesc()
+    d.B, d.T, d.H, d.d_k, d.d_v, d.chunk = B, T, H, dk_, v.shape[-1], chunk
+    d.in_dtype = _dtype(q)
+    d.q, d.k, d.v, d.g, d.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
+    d.S0, d.dO, d.dS_final = _ptr(S0), _ptr(dO), _ptr(dS_final)
+    d.dq, d.dk, d.dv, d.dg, d.dbeta, d.dS0 = (_ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), _ptr(dbeta),
+                                              _ptr(dS0))
+    if workspace is not None:
+        d.workspace, d.workspace_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
+    return d
+
+
+def kda_backward_workspace_size(q, k, v, g, beta, dO, chunk=64) -> int:
+    """Workspace bytes kda_prefill_backward needs for these arguments."""
+    d = _backward_desc(q, k, v, g, beta, dO, chunk=chunk)
+    n = C.c_size_t(0)
+    _check("kda_backward_workspace_size", load().kda_backward_workspace_size(C.byref(d), C.byref(n)))
+    return int(n.value)
+
+
+def kda_prefill_backward(q, k, v, g, beta, dO, *, dq, dk, dv, dg, dbeta, S0=None, dS_final=None,
+                         dS0=None, chunk=64, workspace=None, stream=None) -> None:
+    """Gradients of the chunkwise prefill into the caller's float32 tensors.
+
+    q, k, v: [B,T,H,128] (float32 or bfloat16, as given to the prefill); g: [B,T,H,128] and
+    beta: [B,T,H] float32; dO: [B,T,H,128] float32 gradient of the raw outputs; S0,
+    dS_final, dS0: [B,H,128,128] float32 or None.  dq, dk, dv, dg: [B,T,H,128] float32;
+    dbeta: [B,T,H] float32.  Without a workspace, one is allocated from torch's caching
+    allocator."""
+    if workspace is None:
+        n = kda_backward_workspace_size(q, k, v, g, beta, dO, chunk=chunk)
+        if n > 0:
+            workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
+    d = _backward_desc(q, k, v, g, beta, dO, dq=dq, dk=dk, dv=dv, dg=dg, dbeta=dbeta, S0=S0,
+                       dS_final=dS_final, dS0=dS0, chunk=chunk, workspace=workspace)
+    _check("kda_prefill_backward", load().kda_prefill_backward(C.byref(d), _stream(stream)))

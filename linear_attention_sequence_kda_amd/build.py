@@ -21,7 +21,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 
-SOURCES = ["api.cpp", "decode.hip", "state_copy.hip", "prefill_prep.hip", "prefill_state.hip"]
+SOURCES = ["api.cpp", "decode.hip", "state_copy.hip", "prefill_prep.hip", "prefill_state.hip",
+           "backward.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -198,6 +198,42 @@ kda_status validate_copy_indexed(const float *dst, int64_t dst_count, const int3
   return KDA_OK;
 }
 
+kda_status validate_backward_sizes(const kda_backward_desc *d) {
+  if (!d) return KDA_ERR_NULL;
+  if (d->B < 0 || d->T < 0 || d->H < 0) return KDA_ERR_SHAPE;
+  if (d->d_k != 128 || d->d_v != 128 || d->chunk != 64) return KDA_ERR_UNSUPPORTED;
+  if (!valid_dtype(d->in_dtype)) return KDA_ERR_UNSUPPORTED;
+  const int64_t n_chunks = (static_cast<int64_t>(d->T) + 63) / 64;
+  if (static_cast<int64_t>(d->B) * d->H * n_chunks >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
+  return KDA_OK;
+}
+
+kda_status validate_backward(const kda_backward_desc *d, size_t *ws) {
+  kda_status st = validate_backward_sizes(d);
+  if (st != KDA_OK) return st;
+  const size_t ntok = static_cast<size_t>(d->B) * d->T * d->H;
+  const size_t nstate = static_cast<size_t>(d->B) * d->H;
+  if (ntok > 0 && (!d->q || !d->k || !d->v || !d->g || !d->beta || !d->dO || !d->dq || !d->dk ||
+                   !d->dv || !d->dg || !d->dbeta))
+    return KDA_ERR_NULL;
+  *ws = kda::backward_workspace_bytes(d->B, d->T, d->H);
+  if (*ws > 0 && (!d->workspace || d->workspace_bytes < *ws)) return KDA_ERR_WORKSPACE;
+  const size_t ie = esize(d->in_dtype), sb = nstate * 128 * 128 * 4, tb = ntok * 128 * 4;
+  struct R { const void *p; size_t n; };
+  const R in[] = {{d->q, ntok * 128 * ie}, {d->k, ntok * 128 * ie}, {d->v, ntok * 128 * ie},
+                  {d->g, tb}, {d->beta, ntok * 4}, {d->S0, d->S0 ? sb : 0}, {d->dO, tb},
+                  {d->dS_final, d->dS_final ? sb : 0}};
+  const R out[] = {{d->dq, tb}, {d->dk, tb}, {d->dv, tb}, {d->dg, tb}, {d->dbeta, ntok * 4},
+                   {d->dS0, d->dS0 ? sb : 0}, {d->workspace, *ws}};
+  for (size_t i = 0; i < sizeof(out) / sizeof(out[0]); ++i) {
+    for (const R &r : in)
+      if (overlap(out[i].p, out[i].n, r.p, r.n)) return KDA_ERR_ALIAS;
+    for (size_t j = 0; j < i; ++j)
+      if (overlap(out[i].p, out[i].n, out[j].p, out[j].n)) return KDA_ERR_ALIAS;
+  }
+  return KDA_OK;
+}
+
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
 }  // namespace
@@ -274,12 +310,30 @@ kda_status kda_state_rollback(float *state, const float *ckpt, int64_t n_states,
   return from_hip(kda::launch_state_copy(state, ckpt, n_states * d_k * d_v, stream));
 }
 
+kda_status kda_backward_workspace_size(const kda_backward_desc *d, size_t *bytes) {
+  if (!bytes) return KDA_ERR_NULL;
+  kda_status st = validate_backward_sizes(d);
+  if (st != KDA_OK) return st;
+  *bytes = kda::backward_workspace_bytes(d->B, d->T, d->H);
+  return KDA_OK;
+}
+
+kda_status kda_prefill_backward(const kda_backward_desc *d, hipStream_t stream) {
+  size_t ws = 0;
+  kda_status st = validate_backward(d, &ws);
+  if (st != KDA_OK) return st;
+  if (static_cast<int64_t>(d->B) * d->H == 0) return KDA_OK;
+  st = check_device();
+  if (st != KDA_OK) return st;
+  return from_hip(kda::launch_backward(*d, stream));
+}
+
 const char *kda_status_string(kda_status s) {
   switch (s) {
     case KDA_OK: return "ok";
     case KDA_ERR_NULL: return "a required pointer is NULL";
     case KDA_ERR_SHAPE: return "invalid or inconsistent sizes";
-    case KDA_ERR_UNSUPPORTED: return "unsupported configuration (d_k/d_v must be 128; chunk 16 or 64; dtype f32 or bf16)";
+    case KDA_ERR_UNSUPPORTED: return "unsupported configuration (d_k/d_v must be 128; chunk 16 or 64, 64 for the backward; dtype f32 or bf16)";
     case KDA_ERR_WORKSPACE: return "workspace missing or too small";
     case KDA_ERR_ALIAS: return "an output buffer overlaps a buffer it must not overlap";
     case KDA_ERR_DEVICE: return "current HIP device is not gfx950 (MI355X) or cannot be queried";

@@ -1,0 +1,884 @@
+// Backward pass of the chunkwise KDA prefill (gfx950, fp32 arithmetic throughout).
+//
+// The pages fix the forward only (xhh.club tag page 结构: the recurrent form, and the
+// chunkwise form used for training and prefill).  The gradient here is reverse-mode
+// differentiation of that chunkwise form, per 64-token chunk with
+//   gt = min(0, max(-5, g)),  G_t = sum_{u <= t} gt_u (per key channel),  Gam = G_63,
+//   KK[t][j] = sum_i k_ti k_ji e^{G_ti - G_ji}  (j < t),  P[t][j] = same with q_t (j <= t),
+//   M = (I + diag(beta) KK)^-1,  T = M diag(beta),
+//   W = T (k e^G),  U~ = T v,  Q~ = q e^G,  K_dec = k e^{Gam - G},  D = e^{Gam},
+//   U = U~ - W S,  S_next = D S + K_dec^T U,  O = Q~ S + P U.
+// Given dO (gradient of the raw outputs) and dS_T, the chain rule gives, per chunk,
+//   dU = P^T dO + K_dec dS_next,   dS = D dS_next + Q~^T dO - W^T dU      (reverse sweep)
+//   dP = Lower(dO U^T), dQ~ = dO S^T, dW = -dU S^T, dK_dec = U dS_next^T,
+//   dD = rowsum(dS_next * S), dT = dU v^T + dW (k e^G)^T, dv = T^T dU, d(k e^G) = T^T dW,
+//   dbeta_j = sum_t dT[t][j] M[t][j] + sum_i dA[j][i] KK[j][i],
+//   dA = -M^T (dT diag(beta)) M^T (strictly lower),  dKK = diag(beta) dA,
+// and the pairwise terms of dKK and dP into dk, dq and dG, the elementwise terms of
+// Q~, k e^G and K_dec, then dg_u = [-5 <= g_u <= 0] (sum_{t >= u} dG_t + dGam).
+//
+// Pairwise decays e^{G_t - G_j} are factored through the first token of a 16-token block
+// (block start R): for t >= R >= ... each factor stays inside fp32 range because every
+// step's log-decay is at least -5 (15 steps in a block: at most e^75), the same bound the
+// forward's 16-token diagonal tiles rely on.
+//
+// Four kernels:
+//   bwd_prep    one workgroup per chunk: G, K_dec, Q~, P, KK, M, W, U~, D -> record
+//   bwd_fwd     per (sequence, head, 16 value columns): states entering every chunk
+//   bwd_rev     same split, reverse order: dS after every chunk, and dS0
+//   bwd_grad    one workgroup per chunk: dq, dk, dv, dg, dbeta of the chunk's tokens
+#include "internal.h"
+#include "kda_device.h"
+
+namespace kda {
+namespace {
+
+constexpr int D = 128;        // d_k = d_v
+constexpr int C = 64;         // tokens per chunk
+constexpr int LD = D + 4;     // LDS row stride of [C][D] tiles
+constexpr int LS = C + 4;     // LDS row stride of [C][C] tiles
+constexpr int LV = 20;        // LDS row stride of [*][16] column blocks
+
+// per-chunk record, floats
+constexpr int R_G = 0;              // [C][D] G in log2 units
+constexpr int R_KD = R_G + C * D;   // [C][D] K_dec
+constexpr int R_W = R_KD + C * D;   // [C][D] W
+constexpr int R_UT = R_W + C * D;   // [C][D] U~
+constexpr int R_QT = R_UT + C * D;  // [C][D] Q~
+constexpr int R_P = R_QT + C * D;   // [C][C] P (zero above the diagonal)
+constexpr int R_M = R_P + C * C;    // [C][C] M (zero above the diagonal)
+constexpr int R_KK = R_M + C * C;   // [C][C] KK (zero on and above the diagonal)
+constexpr int R_D = R_KK + C * C;   // [D] e^{Gam}
+constexpr int REC = R_D + D;
+
+struct BwdArgs {
+  const void *q, *k, *v;
+  const float *g, *beta, *S0, *dO, *dSf;
+  float *dq, *dk, *dv, *dg, *dbeta, *dS0;
+  float *rec, *sin, *dsa;
+  int B, T, H, NC;
+};
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// One 16-long contraction block: lane group q supplies contraction index 4q+e to the
+// e-th MFMA (the same permutation on both operands).
+__device__ __forceinline__ f32x4 mma16(f32x4 c, float4 a, float4 b) {
+  c = mfma4(a.x, b.x, c);
+  c = mfma4(a.y, b.y, c);
+  c = mfma4(a.z, b.z, c);
+  return mfma4(a.w, b.w, c);
+}
+__device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast<const float4 *>(p); }
+// p[0], p[ld], p[2 ld], p[3 ld]
+__device__ __forceinline__ float4 col4(const float *p, int ld) {
+  return make_float4(p[0], p[ld], p[2 * ld], p[3 * ld]);
+}
+__device__ __forceinline__ float4 neg4(float4 x) { return make_float4(-x.x, -x.y, -x.z, -x.w); }
+__device__ __forceinline__ float4 mul4(float4 a, float4 b) {
+  return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// element offset of token t of chunk c in a [B,T,H,D] array
+__device__ __forceinline__ size_t tok_off(const BwdArgs &a, int b, int h, int t) {
+  return (static_cast<size_t>(b) * a.T + t) * a.H * D + static_cast<size_t>(h) * D;
+}
+
+// ---------------------------------------------------------------------------
+// bwd_prep: per-chunk quantities of the forward (one workgroup of 512 per chunk)
+// ---------------------------------------------------------------------------
+template <bool BF16>
+__global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
+  __shared__ __align__(16) float sG[C * LD];    // G (log2), then beta k e^G
+  __shared__ __align__(16) float sX[C * LD];    // KR = k e^{G - G_R}, then QR, then beta v
+  __shared__ __align__(16) float sY[C * LD];    // KL = k e^{G_R - G}
+  __shared__ __align__(16) float sA[C * LS];    // beta_t KK[t][j]
+  __shared__ __align__(16) float sM[C * LS];    // M
+  __shared__ __align__(16) float sDel[6 * D];   // e^{G_R(a) - G_R(b)}, a > b
+  __shared__ __align__(16) float sGa[4 * D];    // G at the four block starts
+  __shared__ float sBeta[C];
+  __shared__ float sZ[4][16 * 17];
+
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, q = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ch = blockIdx.x, bh = ch / a.NC, c = ch % a.NC, b = bh / a.H, h = bh % a.H;
+  const int t0 = c * C, Tc = min(C, a.T - t0);
+  float *rec = a.rec + static_cast<size_t>(ch) * REC;
+
+  // decays (log2 units) and beta; tokens past the sequence end are zero
+  for (int e = tid; e < C * D / 4; e += 512) {
+    const int t = e >> 5, i = (e & 31) * 4;
+    float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < Tc) gv = ld4(a.g + tok_off(a, b, h, t0 + t) + i);
+    float *d = sG + t * LD + i;
+    d[0] = log2_decay(gv.x); d[1] = log2_decay(gv.y); d[2] = log2_decay(gv.z); d[3] = log2_decay(gv.w);
+  }
+  for (int e = tid; e < C * LS; e += 512) { sA[e] = 0.f; sM[e] = 0.f; }
+  if (tid < C) sBeta[tid] = tid < Tc ? a.beta[(static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h] : 0.f;
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+    for (int t = 0; t < C; ++t) { s += sG[t * LD + tid]; sG[t * LD + tid] = s; }
+  }
+  __syncthreads();
+  if (tid < D) {
+    const int i = tid;
+    for (int blk = 0; blk < 4; ++blk) sGa[blk * D + i] = sG[16 * blk * LD + i];
+    int p = 0;
+    for (int x = 1; x < 4; ++x)
+      for (int y = 0; y < x; ++y, ++p) sDel[p * D + i] = exp2_fast(sG[16 * x * LD + i] - sG[16 * y * LD + i]);
+    rec[R_D + i] = exp2_fast(sG[(C - 1) * LD + i]);
+  }
+  __syncthreads();
+
+  // pass 1: KR, KL, Q~, K_dec, G
+  for (int e = tid; e < C * D / 4; e += 512) {
+    const int t = e >> 5, i = (e & 31) * 4;
+    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+    if (t < Tc) {
+      const size_t o = tok_off(a, b, h, t0 + t) + i;
+      kv = load4<BF16>(a.k, o);
+      qv = load4<BF16>(a.q, o);
+    }
+    const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, qq[4] = {qv.x, qv.y, qv.z, qv.w};
+    float kr[4], kl[4], qt[4], kd[4], gg[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float G = sG[t * LD + i + x], Ga = sGa[(t >> 4) * D + i + x], Gm = sG[(C - 1) * LD + i + x];
+      kr[x] = kk[x] * exp2_fast(G - Ga);
+      kl[x] = kk[x] * exp2_fast(Ga - G);
+      qt[x] = qq[x] * exp2_fast(G);
+      kd[x] = kk[x] * exp2_fast(Gm - G);
+      gg[x] = G;
+    }
+    *reinterpret_cast<float4 *>(sX + t * LD + i) = make_float4(kr[0], kr[1], kr[2], kr[3]);
+    *reinterpret_cast<float4 *>(sY + t * LD + i) = make_float4(kl[0], kl[1], kl[2], kl[3]);
+    *reinterpret_cast<float4 *>(rec + R_QT + t * D + i) = make_float4(qt[0], qt[1], qt[2], qt[3]);
+    *reinterpret_cast<float4 *>(rec + R_KD + t * D + i) = make_float4(kd[0], kd[1], kd[2], kd[3]);
+    *reinterpret_cast<float4 *>(rec + R_G + t * D + i) = make_float4(gg[0], gg[1], gg[2], gg[3]);
+  }
+  // zero tiles above the block diagonal of KK and P
+  for (int e = tid; e < C * C; e += 512) {
+    const int t = e >> 6, j = e & 63;
+    if ((j >> 4) > (t >> 4)) { rec[R_KK + e] = 0.f; rec[R_P + e] = 0.f; }
+  }
+  __syncthreads();
+
+  // KK and P: tile (ta, tb), ta >= tb: rows t of block ta, columns j of block tb,
+  //   sum_i (X_ti e^{G_R(ta) - G_R(tb)}) KL_ji  with X = KR (KK) or QR (P)
+  auto pair_tiles = [&](bool is_p) {
+    for (int tt = w; tt < 10; tt += 8) {   // tiles in the order (0,0) (1,0) (1,1) (2,0) ...
+      const int ta = tt < 1 ? 0 : tt < 3 ? 1 : tt < 6 ? 2 : 3, tb = tt - ta * (ta + 1) / 2;
+      const float *ar = sX + (16 * ta + r) * LD + 4 * q;
+      const float *br = sY + (16 * tb + r) * LD + 4 * q;
+      const float *dl = sDel + (ta * (ta - 1) / 2 + tb) * D + 4 * q;
+      f32x4 acc = zero4();
+#pragma unroll 4
+      for (int k0 = 0; k0 < D; k0 += 16) {
+        float4 av = ld4(ar + k0);
+        if (ta != tb) av = mul4(av, ld4(dl + k0));
+        acc = mma16(acc, av, ld4(br + k0));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = 16 * ta + 4 * q + e, j = 16 * tb + r;
+        if (is_p) {
+          rec[R_P + t * C + j] = j <= t ? acc[e] : 0.f;
+        } else {
+          const float v = j < t ? acc[e] : 0.f;
+          rec[R_KK + t * C + j] = v;
+          sA[t * LS + j] = sBeta[t] * v;
+        }
+      }
+    }
+  };
+  pair_tiles(false);
+  __syncthreads();
+
+  // pass 2: QR over KR; beta k e^G over G (each element by the thread that reads it)
+  for (int e = tid; e < C * D / 4; e += 512) {
+    const int t = e >> 5, i = (e & 31) * 4;
+    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
+    if (t < Tc) {
+      const size_t o = tok_off(a, b, h, t0 + t) + i;
+      kv = load4<BF16>(a.k, o);
+      qv = load4<BF16>(a.q, o);
+    }
+    const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, qq[4] = {qv.x, qv.y, qv.z, qv.w};
+    const float bt = sBeta[t];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const float G = sG[t * LD + i + x], Ga = sGa[(t >> 4) * D + i + x];
+      sX[t * LD + i + x] = qq[x] * exp2_fast(G - Ga);
+      sG[t * LD + i + x] = bt * kk[x] * exp2_fast(G);
+    }
+  }
+  __syncthreads();
+  pair_tiles(true);
+
+  // M = (I + A)^-1, A = diag(beta) KK strictly lower: 16x16 diagonal blocks by
+  // forward substitution (one wave per block, lane = column), then the blocks below
+  //   M_xy = -M_xx sum_{y <= z < x} A_xz M_zy
+  if (w < 4) {
+    const int blk = w, cc = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      float s = t == cc ? 1.f : 0.f;
+#pragma unroll
+      for (int j = 0; j < t; ++j) s -= sA[(16 * blk + t) * LS + 16 * blk + j] * x[j];
+      x[t] = s;
+    }
+    if (lane < 16)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) sM[(16 * blk + t) * LS + 16 * blk + cc] = x[t];
+  }
+  __syncthreads();
+  for (int xb = 1; xb < 4; ++xb) {
+    if (w < xb) {
+      const int yb = w;
+      f32x4 z = zero4();
+      for (int zb = yb; zb < xb; ++zb) {
+        const float4 av = ld4(sA + (16 * xb + r) * LS + 16 * zb + 4 * q);
+        const float4 bv = col4(sM + (16 * zb + 4 * q) * LS + 16 * yb + r, LS);
+        z = mma16(z, av, bv);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sZ[w][(4 * q + e) * 17 + r] = z[e];
+      const float4 av = ld4(sM + (16 * xb + r) * LS + 16 * xb + 4 * q);
+      const float4 bv = col4(&sZ[w][(4 * q) * 17 + r], 17);
+      const f32x4 y = mma16(zero4(), av, bv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sM[(16 * xb + 4 * q + e) * LS + 16 * yb + r] = -y[e];
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < C * C; e += 512) rec[R_M + e] = sM[(e >> 6) * LS + (e & 63)];
+
+  // beta v over QR
+  for (int e = tid; e < C * D / 4; e += 512) {
+    const int t = e >> 5, i = (e & 31) * 4;
+    float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < Tc) vv = load4<BF16>(a.v, tok_off(a, b, h, t0 + t) + i);
+    const float bt = sBeta[t];
+    *reinterpret_cast<float4 *>(sX + t * LD + i) = make_float4(bt * vv.x, bt * vv.y, bt * vv.z, bt * vv.w);
+  }
+  __syncthreads();
+
+  // W = M (beta k e^G), U~ = M (beta v): wave w rows 16(w&3).., column tiles (w>>2)+2i
+  const int tm = w & 3, tn0 = w >> 2;
+  f32x4 accW[4], accU[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { accW[i] = zero4(); accU[i] = zero4(); }
+  for (int k0 = 0; k0 <= 16 * tm; k0 += 16) {    // M[t][j] = 0 for j > t
+    const float4 av = ld4(sM + (16 * tm + r) * LS + k0 + 4 * q);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int n = 16 * (tn0 + 2 * i) + r;
+      accW[i] = mma16(accW[i], av, col4(sG + (k0 + 4 * q) * LD + n, LD));
+      accU[i] = mma16(accU[i], av, col4(sX + (k0 + 4 * q) * LD + n, LD));
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * tm + 4 * q + e, n = 16 * (tn0 + 2 * i) + r;
+      rec[R_W + t * D + n] = accW[i][e];
+      rec[R_UT + t * D + n] = accU[i][e];
+    }
+}
+
+// (sequence, head) and 16-column block of a sweep workgroup.  The eight column blocks of
+// a (sequence, head) share one XCD (workgroups are dealt to XCDs round robin), so the
+// chunk records they all read are fetched into one L2.
+__device__ __forceinline__ bool sweep_unit(int BH, int &bh, int &cb) {
+  const int x = blockIdx.x, xcd = x & 7, slot = x >> 3;
+  bh = (slot >> 3) * 8 + xcd;
+  cb = slot & 7;
+  return bh < BH;
+}
+
+// ---------------------------------------------------------------------------
+// bwd_fwd: states entering every chunk, for 16 value columns of one (sequence, head)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_fwd(BwdArgs a) {
+  __shared__ __align__(16) float sS[D * LV];
+  __shared__ __align__(16) float sU[C * LV];
+  int bh, cb;
+  if (!sweep_unit(a.B * a.H, bh, cb)) return;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, q = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c0 = 16 * cb;
+  // state rows 16(w + 4 it) + 4q + e, column c0 + r
+  f32x4 S[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * (w + 4 * it) + 4 * q + e;
+      S[it][e] = a.S0 ? a.S0[(static_cast<size_t>(bh) * D + i) * D + c0 + r] : 0.f;
+      sS[i * LV + r] = S[it][e];
+    }
+  __syncthreads();
+  for (int c = 0; c < a.NC; ++c) {
+    const size_t ch = static_cast<size_t>(bh) * a.NC + c;
+    const float *rec = a.rec + ch * REC;
+    float *sin = a.sin + ch * D * D;
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sin[(16 * (w + 4 * it) + 4 * q + e) * D + c0 + r] = S[it][e];
+    // U = U~ - W S, rows 16w..
+    f32x4 acc = zero4();
+    const float *wr = rec + R_W + (16 * w + r) * D + 4 * q;
+#pragma unroll 4
+    for (int k0 = 0; k0 < D; k0 += 16) acc = mma16(acc, ld4(wr + k0), col4(sS + (k0 + 4 * q) * LV + r, LV));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * w + 4 * q + e;
+      sU[t * LV + r] = rec[R_UT + t * D + c0 + r] - acc[e];
+    }
+    __syncthreads();
+    // S = D S + K_dec^T U
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int ib = 16 * (w + 4 * it);
+      f32x4 s;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] = rec[R_D + ib + 4 * q + e] * S[it][e];
+#pragma unroll 4
+      for (int k0 = 0; k0 < C; k0 += 16)
+        s = mma16(s, col4(rec + R_KD + (k0 + 4 * q) * D + ib + r, D), col4(sU + (k0 + 4 * q) * LV + r, LV));
+      S[it] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sS[(16 * (w + 4 * it) + 4 * q + e) * LV + r] = S[it][e];
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// bwd_rev: dS after every chunk (reverse order) and dS0
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
+  __shared__ __align__(16) float sdS[D * LV];
+  __shared__ __align__(16) float sdO[C * LV];
+  __shared__ __align__(16) float sdU[C * LV];
+  int bh, cb;
+  if (!sweep_unit(a.B * a.H, bh, cb)) return;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, q = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c0 = 16 * cb, b = bh / a.H, h = bh % a.H;
+  f32x4 dS[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * (w + 4 * it) + 4 * q + e;
+      dS[it][e] = a.dSf ? a.dSf[(static_cast<size_t>(bh) * D + i) * D + c0 + r] : 0.f;
+      sdS[i * LV + r] = dS[it][e];
+    }
+  for (int c = a.NC - 1; c >= 0; --c) {
+    const size_t ch = static_cast<size_t>(bh) * a.NC + c;
+    const float *rec = a.rec + ch * REC;
+    float *dsa = a.dsa + ch * D * D;
+    const int t0 = c * C, Tc = min(C, a.T - t0);
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsa[(16 * (w + 4 * it) + 4 * q + e) * D + c0 + r] = dS[it][e];
+    for (int e = tid; e < C * 4; e += 256) {
+      const int t = e >> 2, x = (e & 3) * 4;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (t < Tc) v = ld4(a.dO + tok_off(a, b, h, t0 + t) + c0 + x);
+      *reinterpret_cast<float4 *>(sdO + t * LV + x) = v;
+    }
+    __syncthreads();
+    // dU = P^T dO + K_dec dS, rows 16w..  (P^T[t'][t] = 0 for t < t')
+    f32x4 acc = zero4();
+    for (int k0 = 16 * w; k0 < C; k0 += 16)
+      acc = mma16(acc, col4(rec + R_P + (k0 + 4 * q) * C + 16 * w + r, C), col4(sdO + (k0 + 4 * q) * LV + r, LV));
+    const float *kr = rec + R_KD + (16 * w + r) * D + 4 * q;
+#pragma unroll 4
+    for (int k0 = 0; k0 < D; k0 += 16) acc = mma16(acc, ld4(kr + k0), col4(sdS + (k0 + 4 * q) * LV + r, LV));
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sdU[(16 * w + 4 * q + e) * LV + r] = acc[e];
+    __syncthreads();
+    // dS = D dS + Q~^T dO - W^T dU
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int ib = 16 * (w + 4 * it);
+      f32x4 s;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s[e] = rec[R_D + ib + 4 * q + e] * dS[it][e];
+#pragma unroll 2
+      for (int k0 = 0; k0 < C; k0 += 16) {
+        s = mma16(s, col4(rec + R_QT + (k0 + 4 * q) * D + ib + r, D), col4(sdO + (k0 + 4 * q) * LV + r, LV));
+        s = mma16(s, col4(rec + R_W + (k0 + 4 * q) * D + ib + r, D), neg4(col4(sdU + (k0 + 4 * q) * LV + r, LV)));
+      }
+      dS[it] = s;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sdS[(16 * (w + 4 * it) + 4 * q + e) * LV + r] = dS[it][e];
+  }
+  if (a.dS0)
+#pragma unroll
+    for (int it = 0; it < 2; ++it)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        a.dS0[(static_cast<size_t>(bh) * D + 16 * (w + 4 * it) + 4 * q + e) * D + c0 + r] = dS[it][e];
+}
+
+// ---------------------------------------------------------------------------
+// bwd_grad: gradients of one chunk's tokens (one workgroup of 512 per chunk)
+// ---------------------------------------------------------------------------
+// Every [C][D] product below uses one tile map: wave w owns rows 16(w&3)+4q+e and the
+// columns 16((w>>2)+2i)+r, i < 4, so the gradient accumulators dq, dk, dG stay in
+// registers across all of them.  [C][C] products use columns 16((w>>2)+2i)+r, i < 2.
+template <bool BF16>
+__global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
+  __shared__ __align__(16) float s1[C * LD];    // U, then k e^G, then KL; then dG
+  __shared__ __align__(16) float s2[C * LD];    // dU, then KR; then dK_dec * K_dec
+  __shared__ __align__(16) float s3[C * LD];    // dO, then dW, then QR
+  __shared__ __align__(16) float sP[C * LS];    // dP
+  __shared__ __align__(16) float sT[C * LS];    // dT, then dT diag(beta), then dKK
+  __shared__ __align__(16) float sY[C * LS];    // dM M^T
+  __shared__ __align__(16) float sGa[4 * D];    // G at the block starts
+  __shared__ float sBeta[C], sdD[D], sB1[C], sB2[2][C];
+
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, q = lane >> 4;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tm = w & 3, tn0 = w >> 2;
+  const int ch = blockIdx.x, bh = ch / a.NC, c = ch % a.NC, b = bh / a.H, h = bh % a.H;
+  const int t0 = c * C, Tc = min(C, a.T - t0);
+  const float *rec = a.rec + static_cast<size_t>(ch) * REC;
+  const float *S = a.sin + static_cast<size_t>(ch) * D * D;
+  const float *dSn = a.dsa + static_cast<size_t>(ch) * D * D;
+
+  auto row = [&](int e) { return 16 * tm + 4 * q + e; };
+  auto col = [&](int i) { return 16 * (tn0 + 2 * i) + r; };
+
+  // stage dO, beta, block-start G; per-lane G, k, q, Gam
+  for (int e = tid; e < C * D / 4; e += 512) {
+    const int t = e >> 5, i = (e & 31) * 4;
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (t < Tc) v = ld4(a.dO + tok_off(a, b, h, t0 + t) + i);
+    *reinterpret_cast<float4 *>(s3 + t * LD + i) = v;
+  }
+  if (tid < C) sBeta[tid] = tid < Tc ? a.beta[(static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h] : 0.f;
+  sGa[tid] = rec[R_G + 16 * (tid >> 7) * D + (tid & 127)];
+  f32x4 Gr[4], kr[4], qr[4], DQ[4], DK[4], DG[4], KT[4];
+  float Gam[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    Gam[i] = rec[R_G + (C - 1) * D + col(i)];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = row(e);
+      Gr[i][e] = rec[R_G + t * D + col(i)];
+      const size_t o = tok_off(a, b, h, t0 + min(t, Tc - 1)) + col(i);
+      kr[i][e] = t < Tc ? load1<BF16>(a.k, o) : 0.f;
+      qr[i][e] = t < Tc ? load1<BF16>(a.q, o) : 0.f;
+    }
+    DQ[i] = DK[i] = DG[i] = KT[i] = zero4();
+  }
+  // dD = rowsum(dS_next * S): four lanes per row
+  {
+    const int i = tid >> 2, part = tid & 3;
+    float s = 0.f;
+#pragma unroll
+    for (int x = 0; x < 32; x += 4) {
+      const float4 u = ld4(dSn + i * D + 32 * part + x), v = ld4(S + i * D + 32 * part + x);
+      s += u.x * v.x + u.y * v.y + u.z * v.z + u.w * v.w;
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if (part == 0) sdD[i] = s;
+  }
+  __syncthreads();
+
+  f32x4 acc[4];
+  auto clear = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = zero4();
+  };
+
+  // U = U~ - W S  -> s1
+  clear();
+  {
+    const float *ar = rec + R_W + (16 * tm + r) * D + 4 * q;
+#pragma unroll 2
+    for (int k0 = 0; k0 < D; k0 += 16) {
+      const float4 av = ld4(ar + k0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = mma16(acc[i], av, col4(S + (k0 + 4 * q) * D + col(i), D));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s1[row(e) * LD + col(i)] = rec[R_UT + row(e) * D + col(i)] - acc[i][e];
+  }
+  // dU = P^T dO + K_dec dS_next  -> s2
+  clear();
+  {
+    for (int k0 = 16 * tm; k0 < C; k0 += 16) {
+      const float4 av = col4(rec + R_P + (k0 + 4 * q) * C + 16 * tm + r, C);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = mma16(acc[i], av, col4(s3 + (k0 + 4 * q) * LD + col(i), LD));
+    }
+    const float *ar = rec + R_KD + (16 * tm + r) * D + 4 * q;
+#pragma unroll 2
+    for (int k0 = 0; k0 < D; k0 += 16) {
+      const float4 av = ld4(ar + k0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = mma16(acc[i], av, col4(dSn + (k0 + 4 * q) * D + col(i), D));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s2[row(e) * LD + col(i)] = acc[i][e];
+  }
+  // dQ~ = dO S^T: dq += dQ~ e^G, dG += dQ~ * Q~
+  clear();
+  {
+    const float *ar = s3 + (16 * tm + r) * LD + 4 * q;
+#pragma unroll 2
+    for (int k0 = 0; k0 < D; k0 += 16) {
+      const float4 av = ld4(ar + k0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = mma16(acc[i], av, ld4(S + col(i) * D + k0 + 4 * q));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float eg = exp2_fast(Gr[i][e]);
+        DQ[i][e] += acc[i][e] * eg;
+        DG[i][e] += acc[i][e] * qr[i][e] * eg;
+      }
+  }
+  __syncthreads();   // U (s1) and dU (s2) complete
+
+  // dP = Lower(dO U^T)  -> sP
+  {
+    f32x4 p[2] = {zero4(), zero4()};
+    const float *ar = s3 + (16 * tm + r) * LD + 4 * q;
+#pragma unroll 2
+    for (int k0 = 0; k0 < D; k0 += 16) {
+      const float4 av = ld4(ar + k0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (tn0 + 2 * i <= tm) p[i] = mma16(p[i], av, ld4(s1 + col(i) * LD + k0 + 4 * q));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sP[row(e) * LS + col(i)] = col(i) <= row(e) ? p[i][e] : 0.f;
+  }
+  // dK_dec = U dS_next^T: dk += dK_dec e^{Gam - G}; keep dK_dec * K_dec
+  clear();
+  {
+    const float *ar = s1 + (16 * tm + r) * LD + 4 * q;
+#pragma unroll 2
+    for (int k0 = 0; k0 < D; k0 += 16) {
+      const float4 av = ld4(ar + k0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = mma16(acc[i], av, ld4(dSn + col(i) * D + k0 + 4 * q));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f = exp2_fast(Gam[i] - Gr[i][e]);
+        DK[i][e] += acc[i][e] * f;
+        KT[i][e] = acc[i][e] * kr[i][e] * f;
+      }
+  }
+  __syncthreads();   // dO (s3) and U (s1) no longer read
+
+  // dW = -dU S^T -> s3;  k e^G -> s1
+  clear();
+  {
+    const float *ar = s2 + (16 * tm + r) * LD + 4 * q;
+#pragma unroll 2
+    for (int k0 = 0; k0 < D; k0 += 16) {
+      const float4 av = ld4(ar + k0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = mma16(acc[i], av, ld4(S + col(i) * D + k0 + 4 * q));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s3[row(e) * LD + col(i)] = -acc[i][e];
+        s1[row(e) * LD + col(i)] = kr[i][e] * exp2_fast(Gr[i][e]);
+      }
+  }
+  __syncthreads();
+
+  // dT = dU v^T + dW (k e^G)^T -> sT (lower, with the diagonal)
+  {
+    f32x4 p[2] = {zero4(), zero4()};
+    const float *ar = s2 + (16 * tm + r) * LD + 4 * q;
+    const float *aw = s3 + (16 * tm + r) * LD + 4 * q;
+#pragma unroll 2
+    for (int k0 = 0; k0 < D; k0 += 16) {
+      const float4 av = ld4(ar + k0), aw4 = ld4(aw + k0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (tn0 + 2 * i <= tm) {
+          const int j = col(i);
+          float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (j < Tc) vv = load4<BF16>(a.v, tok_off(a, b, h, t0 + j) + k0 + 4 * q);
+          p[i] = mma16(p[i], av, vv);
+          p[i] = mma16(p[i], aw4, ld4(s1 + j * LD + k0 + 4 * q));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sT[row(e) * LS + col(i)] = col(i) <= row(e) ? p[i][e] : 0.f;
+  }
+  // dv = T^T dU (out);  d(k e^G) = T^T dW: dk += . e^G, dG += . k e^G
+  {
+    f32x4 av_acc[4], aw_acc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { av_acc[i] = zero4(); aw_acc[i] = zero4(); }
+    for (int k0 = 16 * tm; k0 < C; k0 += 16) {   // M[t][j] = 0 for t < j
+      const float4 am = col4(rec + R_M + (k0 + 4 * q) * C + 16 * tm + r, C);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        av_acc[i] = mma16(av_acc[i], am, col4(s2 + (k0 + 4 * q) * LD + col(i), LD));
+        aw_acc[i] = mma16(aw_acc[i], am, col4(s3 + (k0 + 4 * q) * LD + col(i), LD));
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int j = row(e);
+      const float bj = sBeta[j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (j < Tc) a.dv[tok_off(a, b, h, t0 + j) + col(i)] = bj * av_acc[i][e];
+        const float eg = exp2_fast(Gr[i][e]), x = bj * aw_acc[i][e];
+        DK[i][e] += x * eg;
+        DG[i][e] += x * kr[i][e] * eg;
+      }
+    }
+  }
+  __syncthreads();   // dT complete
+
+  // dbeta_j, first part: sum_t dT[t][j] M[t][j]; then dT -> dT diag(beta) in place
+  {
+    const int j = tid >> 3, part = tid & 7;
+    float s = 0.f;
+    const float bj = sBeta[j];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int t = 8 * part + x;
+      const float v = sT[t * LS + j];
+      s += v * rec[R_M + t * C + j];
+      sT[t * LS + j] = v * bj;
+    }
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if (part == 0) sB1[j] = s;
+  }
+  __syncthreads();
+  // Y = dM M^T -> sY (only blocks on and below the diagonal are used)
+  {
+    f32x4 p[2] = {zero4(), zero4()};
+    const float *ar = sT + (16 * tm + r) * LS + 4 * q;
+    for (int k0 = 0; k0 < C; k0 += 16) {
+      const float4 av = ld4(ar + k0);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (tn0 + 2 * i <= tm) p[i] = mma16(p[i], av, ld4(rec + R_M + col(i) * C + k0 + 4 * q));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sY[row(e) * LS + col(i)] = p[i][e];
+  }
+  __syncthreads();
+  // dA = -M^T Y (strictly lower): dKK = beta_t dA -> sT; dbeta_t += sum_j dA[t][j] KK[t][j]
+  {
+    f32x4 p[2] = {zero4(), zero4()};
+    for (int k0 = 16 * tm; k0 < C; k0 += 16) {   // M[u][t] = 0 for u < t
+      const float4 am = col4(rec + R_M + (k0 + 4 * q) * C + 16 * tm + r, C);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        if (tn0 + 2 * i <= tm) p[i] = mma16(p[i], am, col4(sY + (k0 + 4 * q) * LS + col(i), LS));
+    }
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int t = row(e), j = col(i);
+        const float da = j < t ? -p[i][e] : 0.f;
+        sT[t * LS + j] = sBeta[t] * da;
+        part[e] += da * rec[R_KK + t * C + j];
+      }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float s = part[e];
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      s += __shfl_xor(s, 4);
+      s += __shfl_xor(s, 8);
+      if (r == 0) sB2[tn0][row(e)] = s;
+    }
+  }
+  // KL -> s1, KR -> s2, QR -> s3 (block start of each row's own 16-token block)
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ga = sGa[tm * D + col(i)], G = Gr[i][e];
+      const float up = exp2_fast(G - ga), dn = exp2_fast(ga - G);
+      s1[row(e) * LD + col(i)] = kr[i][e] * dn;
+      s2[row(e) * LD + col(i)] = kr[i][e] * up;
+      s3[row(e) * LD + col(i)] = qr[i][e] * up;
+    }
+  __syncthreads();
+
+  // pairwise terms, rows t (j in blocks bb <= t's block):
+  //   sum_j dKK[t][j] e^{G_t-G_j} k_j = sum_bb e^{G_t - G_R(bb)} (dKK[t, bb] KL[bb])
+  for (int bb = 0; bb <= tm; ++bb) {
+    f32x4 x[4], y[4];
+    const float4 ak = ld4(sT + (16 * tm + r) * LS + 16 * bb + 4 * q);
+    const float4 ap = ld4(sP + (16 * tm + r) * LS + 16 * bb + 4 * q);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float4 bl = col4(s1 + (16 * bb + 4 * q) * LD + col(i), LD);
+      x[i] = mma16(zero4(), ak, bl);
+      y[i] = mma16(zero4(), ap, bl);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float gr = sGa[bb * D + col(i)];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float f = exp2_fast(fminf(0.f, Gr[i][e] - gr));
+        const float xs = x[i][e] * f, ys = y[i][e] * f;
+        DK[i][e] += xs;
+        DQ[i][e] += ys;
+        DG[i][e] += xs * kr[i][e] + ys * qr[i][e];
+      }
+    }
+  }
+  // rows j (t in blocks aa >= j's block):
+  //   sum_t dKK[t][j] e^{G_t-G_j} k_t = sum_aa e^{G_R(aa) - G_j} (dKK[aa, j]^T KR[aa]), same for dP, q
+  for (int aa = tm; aa < 4; ++aa) {
+    f32x4 x[4];
+    const float4 ak = col4(sT + (16 * aa + 4 * q) * LS + 16 * tm + r, LS);
+    const float4 ap = col4(sP + (16 * aa + 4 * q) * LS + 16 * tm + r, LS);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = mma16(zero4(), ak, col4(s2 + (16 * aa + 4 * q) * LD + col(i), LD));
+      x[i] = mma16(x[i], ap, col4(s3 + (16 * aa + 4 * q) * LD + col(i), LD));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float gr = sGa[aa * D + col(i)];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = x[i][e] * exp2_fast(gr - Gr[i][e]);
+        DK[i][e] += v;
+        DG[i][e] -= v * kr[i][e];
+      }
+    }
+  }
+  __syncthreads();   // s1, s2 free
+
+  // outputs dq, dk; dG - dK_dec*K_dec -> s1, dK_dec*K_dec -> s2
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = row(e);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (t < Tc) {
+        const size_t o = tok_off(a, b, h, t0 + t) + col(i);
+        a.dq[o] = DQ[i][e];
+        a.dk[o] = DK[i][e];
+      }
+      s1[t * LD + col(i)] = DG[i][e] - KT[i][e];
+      s2[t * LD + col(i)] = KT[i][e];
+    }
+  }
+  __syncthreads();
+  if (tid < D) {
+    // dGam = sum_t dK_dec*K_dec + dD e^{Gam};  dg_u = mask_u (sum_{t >= u} dG_t + dGam)
+    const int i = tid;
+    float s = sdD[i] * rec[R_D + i];
+    for (int t = 0; t < C; ++t) s += s2[t * LD + i];
+    for (int u = C - 1; u >= 0; --u) {
+      s += s1[u * LD + i];
+      if (u < Tc) {
+        const size_t o = tok_off(a, b, h, t0 + u) + i;
+        const float g = a.g[o];
+        a.dg[o] = (g >= kFloor && g <= 0.f) ? s : 0.f;
+      }
+    }
+  } else if (tid >= 256 && tid < 256 + C) {
+    const int t = tid - 256;
+    if (t < Tc) a.dbeta[(static_cast<size_t>(b) * a.T + t0 + t) * a.H + h] = sB1[t] + sB2[0][t] + sB2[1][t];
+  }
+}
+
+}  // namespace
+
+size_t backward_workspace_bytes(int B, int T, int H) {
+  const size_t nc = T > 0 ? (static_cast<size_t>(T) + C - 1) / C : 0;
+  return static_cast<size_t>(B) * H * nc * (static_cast<size_t>(REC) + 2 * D * D) * sizeof(float);
+}
+
+hipError_t launch_backward(const kda_backward_desc &d, hipStream_t s) {
+  BwdArgs a;
+  a.q = d.q; a.k = d.k; a.v = d.v; a.g = d.g; a.beta = d.beta; a.S0 = d.S0;
+  a.dO = d.dO; a.dSf = d.dS_final;
+  a.dq = d.dq; a.dk = d.dk; a.dv = d.dv; a.dg = d.dg; a.dbeta = d.dbeta; a.dS0 = d.dS0;
+  a.B = d.B; a.T = d.T; a.H = d.H;
+  a.NC = d.T > 0 ? (d.T + C - 1) / C : 0;
+  const size_t nch = static_cast<size_t>(d.B) * d.H * a.NC;
+  float *ws = static_cast<float *>(d.workspace);
+  a.rec = ws;
+  a.sin = ws + nch * REC;
+  a.dsa = a.sin + nch * D * D;
+  const int BH = d.B * d.H;
+  if (BH == 0) return hipSuccess;
+  const bool bf16 = d.in_dtype == KDA_BF16;
+  if (nch > 0) {
+    if (bf16) bwd_prep<true><<<dim3(static_cast<unsigned>(nch)), dim3(512), 0, s>>>(a);
+    else bwd_prep<false><<<dim3(static_cast<unsigned>(nch)), dim3(512), 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const unsigned sweep_grid = static_cast<unsigned>((BH + 7) / 8 * 64);
+  if (nch > 0) {
+    bwd_fwd<<<dim3(sweep_grid), dim3(256), 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  bwd_rev<<<dim3(sweep_grid), dim3(256), 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (nch > 0) {
+    if (bf16) bwd_grad<true><<<dim3(static_cast<unsigned>(nch)), dim3(512), 0, s>>>(a);
+    else bwd_grad<false><<<dim3(static_cast<unsigned>(nch)), dim3(512), 0, s>>>(a);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace kda

@@ -43,4 +43,9 @@ hipError_t launch_prefill_prep(const kda_prefill_desc &d, int n_chunks, void *re
 
 hipError_t launch_prefill(const kda_prefill_desc &d, const PrefillPlan &p, hipStream_t s);
 
+// Backward pass: workspace bytes, and the four kernels (chunk quantities, state sweep,
+// gradient sweep, per-chunk gradients) on the stream.
+size_t backward_workspace_bytes(int B, int T, int H);
+hipError_t launch_backward(const kda_backward_desc &d, hipStream_t s);
+
 }  // namespace kda

@@ -23,7 +23,8 @@ def test_header_declares_entry_points():
     names = _declared()
     for n in ("kda_prefill_chunked", "kda_decode_step", "kda_decode_step_pooled",
               "kda_state_checkpoint", "kda_state_rollback", "kda_state_copy_indexed",
-              "kda_prefill_workspace_size", "kda_status_string", "kda_abi_version"):
+              "kda_prefill_workspace_size", "kda_status_string", "kda_abi_version",
+              "kda_prefill_backward", "kda_backward_workspace_size"):
         assert n in names
 
 
@@ -34,7 +35,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert kda.kda_abi_version() == 2
+    assert kda.kda_abi_version() == 3
     seen = set()
     for st in range(8):
         s = kda.status_string(st)
@@ -181,3 +182,53 @@ def test_indexed_copy_validation_errors():
     # with slot arrays, counts only bound the slots (checked on the device)
     assert f(None, FAKE, 2, None, FAKE, 2, 0, S, None) == kda.KDA_OK   # nothing to copy
     assert f(FAKE, FAKE + 64, 1, FAKE + (1 << 34), None, 1 << 40, 1 << 30, 1 << 20, None) == kda.KDA_ERR_SHAPE
+
+
+def _bdesc(**over):
+    d = _lib.BackwardDesc()
+    d.B, d.T, d.H, d.d_k, d.d_v, d.chunk, d.in_dtype = 2, 100, 3, 128, 128, 64, _lib.KDA_BF16
+    n = 2 * 100 * 3 * 128 * 4          # bytes of one fp32 [B,T,H,128] array
+    base = FAKE
+    d.q, d.k, d.v, d.g, d.beta, d.dO = (base + i * n for i in range(6))
+    d.dq, d.dk, d.dv, d.dg, d.dbeta = (base + (10 + i) * n for i in range(5))
+    d.workspace, d.workspace_bytes = base + 20 * n, 1 << 30
+    for k, v in over.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_backward_workspace_size():
+    lib = _lib.load()
+    n = C.c_size_t(0)
+    assert lib.kda_backward_workspace_size(C.byref(_bdesc()), C.byref(n)) == kda.KDA_OK
+    # 2 chunks per sequence (T = 100), 2 x 3 heads: record + state + state gradient
+    rec = 5 * 64 * 128 + 3 * 64 * 64 + 128
+    assert n.value == 2 * 3 * 2 * (rec + 2 * 128 * 128) * 4
+    assert lib.kda_backward_workspace_size(C.byref(_bdesc(T=0)), C.byref(n)) == kda.KDA_OK
+    assert n.value == 0
+    assert lib.kda_backward_workspace_size(C.byref(_bdesc(chunk=16)), C.byref(n)) == kda.KDA_ERR_UNSUPPORTED
+    assert lib.kda_backward_workspace_size(None, C.byref(n)) == kda.KDA_ERR_NULL
+
+
+def test_backward_validation_errors():
+    lib = _lib.load()
+    f = lambda d: lib.kda_prefill_backward(C.byref(d), None)  # noqa: E731
+    assert lib.kda_prefill_backward(None, None) == kda.KDA_ERR_NULL
+    assert f(_bdesc(d_k=64)) == kda.KDA_ERR_UNSUPPORTED
+    assert f(_bdesc(chunk=16)) == kda.KDA_ERR_UNSUPPORTED
+    assert f(_bdesc(in_dtype=7)) == kda.KDA_ERR_UNSUPPORTED
+    assert f(_bdesc(T=-1)) == kda.KDA_ERR_SHAPE
+    assert f(_bdesc(dO=None)) == kda.KDA_ERR_NULL
+    assert f(_bdesc(dbeta=None)) == kda.KDA_ERR_NULL
+    assert f(_bdesc(workspace=None)) == kda.KDA_ERR_WORKSPACE
+    assert f(_bdesc(workspace_bytes=1000)) == kda.KDA_ERR_WORKSPACE
+    d = _bdesc()
+    d.dq = d.k                                   # output over an input
+    assert f(d) == kda.KDA_ERR_ALIAS
+    d = _bdesc()
+    d.dg = d.dk + 64                             # two outputs overlap
+    assert f(d) == kda.KDA_ERR_ALIAS
+    d = _bdesc()
+    d.workspace = d.dv                           # workspace over an output
+    assert f(d) == kda.KDA_ERR_ALIAS
+    assert f(_bdesc(B=0)) == kda.KDA_OK          # nothing to do
