@@ -24,8 +24,8 @@
 //
 // Four kernels:
 //   bwd_prep    one workgroup per chunk: G, K_dec, Q~, P, KK, M, W, U~, D -> record
-//   bwd_fwd     per (sequence, head, 16 value columns): states entering every chunk
-//   bwd_rev     same split, reverse order: dS after every chunk, and dS0
+//   bwd_fwd     per (sequence, head, 16 value columns): states entering every chunk, U
+//   bwd_rev     same split, reverse order: dS after every chunk, dU, and dS0
 //   bwd_grad    one workgroup per chunk: dq, dk, dv, dg, dbeta of the chunk's tokens
 #include "internal.h"
 #include "kda_device.h"
@@ -43,7 +43,7 @@ constexpr int LV = 20;        // LDS row stride of [*][16] column blocks
 constexpr int R_G = 0;              // [C][D] G in log2 units
 constexpr int R_KD = R_G + C * D;   // [C][D] K_dec
 constexpr int R_W = R_KD + C * D;   // [C][D] W
-constexpr int R_UT = R_W + C * D;   // [C][D] U~
+constexpr int R_UT = R_W + C * D;   // [C][D] U~, replaced by U = U~ - W S in the state sweep
 constexpr int R_QT = R_UT + C * D;  // [C][D] Q~
 constexpr int R_P = R_QT + C * D;   // [C][C] P (zero above the diagonal)
 constexpr int R_M = R_P + C * C;    // [C][C] M (zero above the diagonal)
@@ -55,7 +55,7 @@ struct BwdArgs {
   const void *q, *k, *v;
   const float *g, *beta, *S0, *dO, *dSf;
   float *dq, *dk, *dv, *dg, *dbeta, *dS0;
-  float *rec, *sin, *dsa;
+  float *rec, *sin, *dsa, *du;
   int B, T, H, NC;
 };
 
@@ -86,6 +86,16 @@ __device__ __forceinline__ size_t tok_off(const BwdArgs &a, int b, int h, int t)
   return (static_cast<size_t>(b) * a.T + t) * a.H * D + static_cast<size_t>(h) * D;
 }
 
+// Barrier that orders LDS accesses only: it waits for this wave's LDS operations, not for
+// its global loads in flight (the prefetches of the next phase) nor its global stores.
+// The kernels below never read global memory they write, so LDS is all a barrier orders.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // bwd_prep: per-chunk quantities of the forward (one workgroup of 512 per chunk)
 // ---------------------------------------------------------------------------
@@ -108,21 +118,29 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
   float *rec = a.rec + static_cast<size_t>(ch) * REC;
 
   // decays (log2 units) and beta; tokens past the sequence end are zero
-  for (int e = tid; e < C * D / 4; e += 512) {
-    const int t = e >> 5, i = (e & 31) * 4;
-    float4 gv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < Tc) gv = ld4(a.g + tok_off(a, b, h, t0 + t) + i);
-    float *d = sG + t * LD + i;
-    d[0] = log2_decay(gv.x); d[1] = log2_decay(gv.y); d[2] = log2_decay(gv.z); d[3] = log2_decay(gv.w);
+  {
+    float4 gv[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
+      gv[x] = ld4(a.g + tok_off(a, b, h, t0 + min(t, Tc - 1)) + i);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
+      if (t >= Tc) gv[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+      float *d = sG + t * LD + i;
+      d[0] = log2_decay(gv[x].x); d[1] = log2_decay(gv[x].y); d[2] = log2_decay(gv[x].z); d[3] = log2_decay(gv[x].w);
+    }
   }
   for (int e = tid; e < C * LS; e += 512) { sA[e] = 0.f; sM[e] = 0.f; }
   if (tid < C) sBeta[tid] = tid < Tc ? a.beta[(static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h] : 0.f;
-  __syncthreads();
+  lds_barrier();
   if (tid < D) {
     float s = 0.f;
     for (int t = 0; t < C; ++t) { s += sG[t * LD + tid]; sG[t * LD + tid] = s; }
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < D) {
     const int i = tid;
     for (int blk = 0; blk < 4; ++blk) sGa[blk * D + i] = sG[16 * blk * LD + i];
@@ -131,27 +149,31 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
       for (int y = 0; y < x; ++y, ++p) sDel[p * D + i] = exp2_fast(sG[16 * x * LD + i] - sG[16 * y * LD + i]);
     rec[R_D + i] = exp2_fast(sG[(C - 1) * LD + i]);
   }
-  __syncthreads();
+  lds_barrier();
 
-  // pass 1: KR, KL, Q~, K_dec, G
-  for (int e = tid; e < C * D / 4; e += 512) {
-    const int t = e >> 5, i = (e & 31) * 4;
-    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
-    if (t < Tc) {
-      const size_t o = tok_off(a, b, h, t0 + t) + i;
-      kv = load4<BF16>(a.k, o);
-      qv = load4<BF16>(a.q, o);
-    }
-    const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, qq[4] = {qv.x, qv.y, qv.z, qv.w};
+  // pass 1: KR, KL, Q~, K_dec, G; k and q stay in registers for pass 2
+  float4 kv[4], qv[4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
+    const size_t o = tok_off(a, b, h, t0 + min(t, Tc - 1)) + i;
+    kv[x] = load4<BF16>(a.k, o);
+    qv[x] = load4<BF16>(a.q, o);
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
+    if (t >= Tc) { kv[x] = make_float4(0.f, 0.f, 0.f, 0.f); qv[x] = kv[x]; }
+    const float kk[4] = {kv[x].x, kv[x].y, kv[x].z, kv[x].w}, qq[4] = {qv[x].x, qv[x].y, qv[x].z, qv[x].w};
     float kr[4], kl[4], qt[4], kd[4], gg[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const float G = sG[t * LD + i + x], Ga = sGa[(t >> 4) * D + i + x], Gm = sG[(C - 1) * LD + i + x];
-      kr[x] = kk[x] * exp2_fast(G - Ga);
-      kl[x] = kk[x] * exp2_fast(Ga - G);
-      qt[x] = qq[x] * exp2_fast(G);
-      kd[x] = kk[x] * exp2_fast(Gm - G);
-      gg[x] = G;
+    for (int y = 0; y < 4; ++y) {
+      const float G = sG[t * LD + i + y], Ga = sGa[(t >> 4) * D + i + y], Gm = sG[(C - 1) * LD + i + y];
+      kr[y] = kk[y] * exp2_fast(G - Ga);
+      kl[y] = kk[y] * exp2_fast(Ga - G);
+      qt[y] = qq[y] * exp2_fast(G);
+      kd[y] = kk[y] * exp2_fast(Gm - G);
+      gg[y] = G;
     }
     *reinterpret_cast<float4 *>(sX + t * LD + i) = make_float4(kr[0], kr[1], kr[2], kr[3]);
     *reinterpret_cast<float4 *>(sY + t * LD + i) = make_float4(kl[0], kl[1], kl[2], kl[3]);
@@ -164,7 +186,7 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
     const int t = e >> 6, j = e & 63;
     if ((j >> 4) > (t >> 4)) { rec[R_KK + e] = 0.f; rec[R_P + e] = 0.f; }
   }
-  __syncthreads();
+  lds_barrier();
 
   // KK and P: tile (ta, tb), ta >= tb: rows t of block ta, columns j of block tb,
   //   sum_i (X_ti e^{G_R(ta) - G_R(tb)}) KL_ji  with X = KR (KK) or QR (P)
@@ -195,27 +217,22 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
     }
   };
   pair_tiles(false);
-  __syncthreads();
+  lds_barrier();
 
   // pass 2: QR over KR; beta k e^G over G (each element by the thread that reads it)
-  for (int e = tid; e < C * D / 4; e += 512) {
-    const int t = e >> 5, i = (e & 31) * 4;
-    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), qv = kv;
-    if (t < Tc) {
-      const size_t o = tok_off(a, b, h, t0 + t) + i;
-      kv = load4<BF16>(a.k, o);
-      qv = load4<BF16>(a.q, o);
-    }
-    const float kk[4] = {kv.x, kv.y, kv.z, kv.w}, qq[4] = {qv.x, qv.y, qv.z, qv.w};
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
+    const float kk[4] = {kv[x].x, kv[x].y, kv[x].z, kv[x].w}, qq[4] = {qv[x].x, qv[x].y, qv[x].z, qv[x].w};
     const float bt = sBeta[t];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const float G = sG[t * LD + i + x], Ga = sGa[(t >> 4) * D + i + x];
-      sX[t * LD + i + x] = qq[x] * exp2_fast(G - Ga);
-      sG[t * LD + i + x] = bt * kk[x] * exp2_fast(G);
+    for (int y = 0; y < 4; ++y) {
+      const float G = sG[t * LD + i + y], Ga = sGa[(t >> 4) * D + i + y];
+      sX[t * LD + i + y] = qq[y] * exp2_fast(G - Ga);
+      sG[t * LD + i + y] = bt * kk[y] * exp2_fast(G);
     }
   }
-  __syncthreads();
+  lds_barrier();
   pair_tiles(true);
 
   // M = (I + A)^-1, A = diag(beta) KK strictly lower: 16x16 diagonal blocks by
@@ -235,7 +252,7 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
 #pragma unroll
       for (int t = 0; t < 16; ++t) sM[(16 * blk + t) * LS + 16 * blk + cc] = x[t];
   }
-  __syncthreads();
+  lds_barrier();
   for (int xb = 1; xb < 4; ++xb) {
     if (w < xb) {
       const int yb = w;
@@ -253,19 +270,26 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) sM[(16 * xb + 4 * q + e) * LS + 16 * yb + r] = -y[e];
     }
-    __syncthreads();
+    lds_barrier();
   }
   for (int e = tid; e < C * C; e += 512) rec[R_M + e] = sM[(e >> 6) * LS + (e & 63)];
 
   // beta v over QR
-  for (int e = tid; e < C * D / 4; e += 512) {
-    const int t = e >> 5, i = (e & 31) * 4;
-    float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < Tc) vv = load4<BF16>(a.v, tok_off(a, b, h, t0 + t) + i);
-    const float bt = sBeta[t];
-    *reinterpret_cast<float4 *>(sX + t * LD + i) = make_float4(bt * vv.x, bt * vv.y, bt * vv.z, bt * vv.w);
+  {
+    float4 vv[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
+      vv[x] = load4<BF16>(a.v, tok_off(a, b, h, t0 + min(t, Tc - 1)) + i);
+    }
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
+      const float bt = sBeta[t];   // zero past the sequence end
+      *reinterpret_cast<float4 *>(sX + t * LD + i) = make_float4(bt * vv[x].x, bt * vv[x].y, bt * vv[x].z, bt * vv[x].w);
+    }
   }
-  __syncthreads();
+  lds_barrier();
 
   // W = M (beta k e^G), U~ = M (beta v): wave w rows 16(w&3).., column tiles (w>>2)+2i
   const int tm = w & 3, tn0 = w >> 2;
@@ -304,6 +328,12 @@ __device__ __forceinline__ bool sweep_unit(int BH, int &bh, int &cb) {
 // ---------------------------------------------------------------------------
 // bwd_fwd: states entering every chunk, for 16 value columns of one (sequence, head)
 // ---------------------------------------------------------------------------
+// Each chunk step has two phases, U = U~ - W S (rows 16w.. of U) and S = D S + K_dec^T U
+// (state rows 16(w + 4 it)..); the record fragments of a phase are loaded one phase
+// ahead, for the next chunk, so their latency overlaps the other phase.
+struct FwdA { float4 w[8]; float ut[4]; };
+struct FwdB { float kd[2][4][4]; float d[2][4]; };
+
 __global__ __launch_bounds__(256) void bwd_fwd(BwdArgs a) {
   __shared__ __align__(16) float sS[D * LV];
   __shared__ __align__(16) float sU[C * LV];
@@ -312,6 +342,27 @@ __global__ __launch_bounds__(256) void bwd_fwd(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, q = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = 16 * cb;
+  float *recs = a.rec + static_cast<size_t>(bh) * a.NC * REC;
+  auto loadA = [&](FwdA &x, int c) {
+    const float *rec = recs + static_cast<size_t>(c) * REC;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) x.w[kb] = ld4(rec + R_W + (16 * w + r) * D + 16 * kb + 4 * q);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x.ut[e] = rec[R_UT + (16 * w + 4 * q + e) * D + c0 + r];
+  };
+  auto loadB = [&](FwdB &x, int c) {
+    const float *rec = recs + static_cast<size_t>(c) * REC;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int ib = 16 * (w + 4 * it);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x.kd[it][kb][e] = rec[R_KD + (16 * kb + 4 * q + e) * D + ib + r];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x.d[it][e] = rec[R_D + ib + 4 * q + e];
+    }
+  };
   // state rows 16(w + 4 it) + 4q + e, column c0 + r
   f32x4 S[2];
 #pragma unroll
@@ -322,50 +373,62 @@ __global__ __launch_bounds__(256) void bwd_fwd(BwdArgs a) {
       S[it][e] = a.S0 ? a.S0[(static_cast<size_t>(bh) * D + i) * D + c0 + r] : 0.f;
       sS[i * LV + r] = S[it][e];
     }
+  FwdA A;
+  FwdB Bf;
+  loadA(A, 0);
+  loadB(Bf, 0);
   __syncthreads();
   for (int c = 0; c < a.NC; ++c) {
-    const size_t ch = static_cast<size_t>(bh) * a.NC + c;
-    const float *rec = a.rec + ch * REC;
-    float *sin = a.sin + ch * D * D;
+    const int cn = min(c + 1, a.NC - 1);   // the last step reloads its own chunk
+    float *sin = a.sin + (static_cast<size_t>(bh) * a.NC + c) * D * D;
 #pragma unroll
     for (int it = 0; it < 2; ++it)
 #pragma unroll
       for (int e = 0; e < 4; ++e) sin[(16 * (w + 4 * it) + 4 * q + e) * D + c0 + r] = S[it][e];
     // U = U~ - W S, rows 16w..
     f32x4 acc = zero4();
-    const float *wr = rec + R_W + (16 * w + r) * D + 4 * q;
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 16) acc = mma16(acc, ld4(wr + k0), col4(sS + (k0 + 4 * q) * LV + r, LV));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int kb = 0; kb < 8; ++kb) acc = mma16(acc, A.w[kb], col4(sS + (16 * kb + 4 * q) * LV + r, LV));
+    float *rec = recs + static_cast<size_t>(c) * REC;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {   // U replaces U~ (its columns are this workgroup's alone)
       const int t = 16 * w + 4 * q + e;
-      sU[t * LV + r] = rec[R_UT + t * D + c0 + r] - acc[e];
+      const float u = A.ut[e] - acc[e];
+      sU[t * LV + r] = u;
+      rec[R_UT + t * D + c0 + r] = u;
     }
-    __syncthreads();
+    loadA(A, cn);
+    lds_barrier();
     // S = D S + K_dec^T U
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-      const int ib = 16 * (w + 4 * it);
       f32x4 s;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[e] = rec[R_D + ib + 4 * q + e] * S[it][e];
-#pragma unroll 4
-      for (int k0 = 0; k0 < C; k0 += 16)
-        s = mma16(s, col4(rec + R_KD + (k0 + 4 * q) * D + ib + r, D), col4(sU + (k0 + 4 * q) * LV + r, LV));
+      for (int e = 0; e < 4; ++e) s[e] = Bf.d[it][e] * S[it][e];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        s = mma16(s, make_float4(Bf.kd[it][kb][0], Bf.kd[it][kb][1], Bf.kd[it][kb][2], Bf.kd[it][kb][3]),
+                  col4(sU + (16 * kb + 4 * q) * LV + r, LV));
       S[it] = s;
     }
-    __syncthreads();
+    loadB(Bf, cn);
+    lds_barrier();
 #pragma unroll
     for (int it = 0; it < 2; ++it)
 #pragma unroll
       for (int e = 0; e < 4; ++e) sS[(16 * (w + 4 * it) + 4 * q + e) * LV + r] = S[it][e];
-    __syncthreads();
+    lds_barrier();
   }
 }
 
 // ---------------------------------------------------------------------------
 // bwd_rev: dS after every chunk (reverse order) and dS0
 // ---------------------------------------------------------------------------
+// Phases dU = P^T dO + K_dec dS (rows 16w..) and dS = D dS + Q~^T dO - W^T dU, with the
+// record fragments and the dO block of the next (earlier) chunk loaded one phase ahead.
+struct RevA { float p[4][4]; float4 kd[8]; };
+struct RevB { float qt[2][4][4]; float wt[2][4][4]; float d[2][4]; };
+
 __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
   __shared__ __align__(16) float sdS[D * LV];
   __shared__ __align__(16) float sdO[C * LV];
@@ -375,6 +438,40 @@ __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, q = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c0 = 16 * cb, b = bh / a.H, h = bh % a.H;
+  const float *recs = a.rec + static_cast<size_t>(bh) * a.NC * REC;
+  auto loadA = [&](RevA &x, int c) {
+    const float *rec = recs + static_cast<size_t>(c) * REC;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)   // P^T[t'][t] (zero for t < t')
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x.p[kb][e] = rec[R_P + (16 * kb + 4 * q + e) * C + 16 * w + r];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) x.kd[kb] = ld4(rec + R_KD + (16 * w + r) * D + 16 * kb + 4 * q);
+  };
+  auto loadB = [&](RevB &x, int c) {
+    const float *rec = recs + static_cast<size_t>(c) * REC;
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int ib = 16 * (w + 4 * it);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x.qt[it][kb][e] = rec[R_QT + (16 * kb + 4 * q + e) * D + ib + r];
+          x.wt[it][kb][e] = rec[R_W + (16 * kb + 4 * q + e) * D + ib + r];
+        }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x.d[it][e] = rec[R_D + ib + 4 * q + e];
+    }
+  };
+  // one float4 of the chunk's dO block [64][16] per thread (rows past the end read 0)
+  const int ot = tid >> 2, ox = (tid & 3) * 4;
+  auto loadO = [&](int c) {
+    const int t = c * C + ot;
+    float4 v = ld4(a.dO + tok_off(a, b, h, min(t, a.T - 1)) + c0 + ox);
+    if (t >= a.T) v = make_float4(0.f, 0.f, 0.f, 0.f);
+    return v;
+  };
   f32x4 dS[2];
 #pragma unroll
   for (int it = 0; it < 2; ++it)
@@ -384,51 +481,60 @@ __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
       dS[it][e] = a.dSf ? a.dSf[(static_cast<size_t>(bh) * D + i) * D + c0 + r] : 0.f;
       sdS[i * LV + r] = dS[it][e];
     }
-  for (int c = a.NC - 1; c >= 0; --c) {
-    const size_t ch = static_cast<size_t>(bh) * a.NC + c;
-    const float *rec = a.rec + ch * REC;
-    float *dsa = a.dsa + ch * D * D;
-    const int t0 = c * C, Tc = min(C, a.T - t0);
+  if (a.NC > 0) {
+    RevA A;
+    RevB Bf;
+    float4 ov = loadO(a.NC - 1);
+    loadA(A, a.NC - 1);
+    loadB(Bf, a.NC - 1);
+    for (int c = a.NC - 1; c >= 0; --c) {
+      const int cn = max(c - 1, 0);   // the last step reloads its own chunk
+      float *dsa = a.dsa + (static_cast<size_t>(bh) * a.NC + c) * D * D;
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
+      for (int it = 0; it < 2; ++it)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dsa[(16 * (w + 4 * it) + 4 * q + e) * D + c0 + r] = dS[it][e];
-    for (int e = tid; e < C * 4; e += 256) {
-      const int t = e >> 2, x = (e & 3) * 4;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (t < Tc) v = ld4(a.dO + tok_off(a, b, h, t0 + t) + c0 + x);
-      *reinterpret_cast<float4 *>(sdO + t * LV + x) = v;
-    }
-    __syncthreads();
-    // dU = P^T dO + K_dec dS, rows 16w..  (P^T[t'][t] = 0 for t < t')
-    f32x4 acc = zero4();
-    for (int k0 = 16 * w; k0 < C; k0 += 16)
-      acc = mma16(acc, col4(rec + R_P + (k0 + 4 * q) * C + 16 * w + r, C), col4(sdO + (k0 + 4 * q) * LV + r, LV));
-    const float *kr = rec + R_KD + (16 * w + r) * D + 4 * q;
-#pragma unroll 4
-    for (int k0 = 0; k0 < D; k0 += 16) acc = mma16(acc, ld4(kr + k0), col4(sdS + (k0 + 4 * q) * LV + r, LV));
+        for (int e = 0; e < 4; ++e) dsa[(16 * (w + 4 * it) + 4 * q + e) * D + c0 + r] = dS[it][e];
+      *reinterpret_cast<float4 *>(sdO + ot * LV + ox) = ov;
+      lds_barrier();
+      ov = loadO(cn);
+      // dU = P^T dO + K_dec dS, rows 16w..
+      f32x4 acc = zero4();
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sdU[(16 * w + 4 * q + e) * LV + r] = acc[e];
-    __syncthreads();
-    // dS = D dS + Q~^T dO - W^T dU
+      for (int kb = 0; kb < 4; ++kb)
+        acc = mma16(acc, make_float4(A.p[kb][0], A.p[kb][1], A.p[kb][2], A.p[kb][3]),
+                    col4(sdO + (16 * kb + 4 * q) * LV + r, LV));
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int ib = 16 * (w + 4 * it);
-      f32x4 s;
+      for (int kb = 0; kb < 8; ++kb) acc = mma16(acc, A.kd[kb], col4(sdS + (16 * kb + 4 * q) * LV + r, LV));
+      float *du = a.du + (static_cast<size_t>(bh) * a.NC + c) * C * D;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[e] = rec[R_D + ib + 4 * q + e] * dS[it][e];
-#pragma unroll 2
-      for (int k0 = 0; k0 < C; k0 += 16) {
-        s = mma16(s, col4(rec + R_QT + (k0 + 4 * q) * D + ib + r, D), col4(sdO + (k0 + 4 * q) * LV + r, LV));
-        s = mma16(s, col4(rec + R_W + (k0 + 4 * q) * D + ib + r, D), neg4(col4(sdU + (k0 + 4 * q) * LV + r, LV)));
+      for (int e = 0; e < 4; ++e) {
+        sdU[(16 * w + 4 * q + e) * LV + r] = acc[e];
+        du[(16 * w + 4 * q + e) * D + c0 + r] = acc[e];
       }
-      dS[it] = s;
+      loadA(A, cn);
+      lds_barrier();
+      // dS = D dS + Q~^T dO - W^T dU
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        f32x4 s;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[e] = Bf.d[it][e] * dS[it][e];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const float4 qv = make_float4(Bf.qt[it][kb][0], Bf.qt[it][kb][1], Bf.qt[it][kb][2], Bf.qt[it][kb][3]);
+          const float4 wv = make_float4(Bf.wt[it][kb][0], Bf.wt[it][kb][1], Bf.wt[it][kb][2], Bf.wt[it][kb][3]);
+          s = mma16(s, qv, col4(sdO + (16 * kb + 4 * q) * LV + r, LV));
+          s = mma16(s, wv, neg4(col4(sdU + (16 * kb + 4 * q) * LV + r, LV)));
+        }
+        dS[it] = s;
+      }
+      loadB(Bf, cn);
+      lds_barrier();
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sdS[(16 * (w + 4 * it) + 4 * q + e) * LV + r] = dS[it][e];
     }
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < 2; ++it)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sdS[(16 * (w + 4 * it) + 4 * q + e) * LV + r] = dS[it][e];
   }
   if (a.dS0)
 #pragma unroll
@@ -446,12 +552,12 @@ __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
 // registers across all of them.  [C][C] products use columns 16((w>>2)+2i)+r, i < 2.
 template <bool BF16>
 __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
-  __shared__ __align__(16) float s1[C * LD];    // U, then k e^G, then KL; then dG
+  __shared__ __align__(16) float s1[C * LD];    // U, then k e^G, then dM M^T, then KL; then dG
   __shared__ __align__(16) float s2[C * LD];    // dU, then KR; then dK_dec * K_dec
   __shared__ __align__(16) float s3[C * LD];    // dO, then dW, then QR
-  __shared__ __align__(16) float sP[C * LS];    // dP
+  __shared__ __align__(16) float sP[C * LS];    // dP; then partial sums of the dg scan
   __shared__ __align__(16) float sT[C * LS];    // dT, then dT diag(beta), then dKK
-  __shared__ __align__(16) float sY[C * LS];    // dM M^T
+  __shared__ __align__(16) float sM[C * LS];    // M
   __shared__ __align__(16) float sGa[4 * D];    // G at the block starts
   __shared__ float sBeta[C], sdD[D], sB1[C], sB2[2][C];
 
@@ -467,15 +573,24 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
   auto row = [&](int e) { return 16 * tm + 4 * q + e; };
   auto col = [&](int i) { return 16 * (tn0 + 2 * i) + r; };
 
-  // stage dO, beta, block-start G; per-lane G, k, q, Gam
-  for (int e = tid; e < C * D / 4; e += 512) {
-    const int t = e >> 5, i = (e & 31) * 4;
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (t < Tc) v = ld4(a.dO + tok_off(a, b, h, t0 + t) + i);
-    *reinterpret_cast<float4 *>(s3 + t * LD + i) = v;
+  // stage dO, U and dU (both written by the sweeps), M, beta, block-start G; every
+  // global load of the staging is issued before the first LDS store
+  const float *Ug = rec + R_UT;   // U~ replaced by U in the state sweep
+  const float *dUg = a.du + static_cast<size_t>(ch) * C * D;
+  const float bt = a.beta[(static_cast<size_t>(b) * a.T + t0 + min(tid & 63, Tc - 1)) * a.H + h];
+  const float ga = rec[R_G + 16 * (tid >> 7) * D + (tid & 127)];
+  float4 vo[4], vu[4], vd[4], vm[2];
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
+    vo[x] = ld4(a.dO + tok_off(a, b, h, t0 + min(t, Tc - 1)) + i);
+    if (t >= Tc) vo[x] = make_float4(0.f, 0.f, 0.f, 0.f);
+    vu[x] = ld4(Ug + t * D + i);
+    vd[x] = ld4(dUg + t * D + i);
   }
-  if (tid < C) sBeta[tid] = tid < Tc ? a.beta[(static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h] : 0.f;
-  sGa[tid] = rec[R_G + 16 * (tid >> 7) * D + (tid & 127)];
+#pragma unroll
+  for (int x = 0; x < 2; ++x) vm[x] = ld4(rec + R_M + 4 * (tid + 512 * x));
+  // per-lane G, k, q at the lane's 16 elements of the tile map, and Gam of its columns
   f32x4 Gr[4], kr[4], qr[4], DQ[4], DK[4], DG[4], KT[4];
   float Gam[4];
 #pragma unroll
@@ -486,87 +601,31 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
       const int t = row(e);
       Gr[i][e] = rec[R_G + t * D + col(i)];
       const size_t o = tok_off(a, b, h, t0 + min(t, Tc - 1)) + col(i);
-      kr[i][e] = t < Tc ? load1<BF16>(a.k, o) : 0.f;
-      qr[i][e] = t < Tc ? load1<BF16>(a.q, o) : 0.f;
+      kr[i][e] = load1<BF16>(a.k, o);
+      qr[i][e] = load1<BF16>(a.q, o);
     }
     DQ[i] = DK[i] = DG[i] = KT[i] = zero4();
   }
-  // dD = rowsum(dS_next * S): four lanes per row
-  {
-    const int i = tid >> 2, part = tid & 3;
-    float s = 0.f;
 #pragma unroll
-    for (int x = 0; x < 32; x += 4) {
-      const float4 u = ld4(dSn + i * D + 32 * part + x), v = ld4(S + i * D + 32 * part + x);
-      s += u.x * v.x + u.y * v.y + u.z * v.z + u.w * v.w;
-    }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    if (part == 0) sdD[i] = s;
+  for (int x = 0; x < 4; ++x) {
+    const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
+    *reinterpret_cast<float4 *>(s3 + t * LD + i) = vo[x];
+    *reinterpret_cast<float4 *>(s1 + t * LD + i) = vu[x];
+    *reinterpret_cast<float4 *>(s2 + t * LD + i) = vd[x];
   }
-  __syncthreads();
-
-  f32x4 acc[4];
-  auto clear = [&]() {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = zero4();
-  };
-
-  // U = U~ - W S  -> s1
-  clear();
-  {
-    const float *ar = rec + R_W + (16 * tm + r) * D + 4 * q;
-#pragma unroll 2
-    for (int k0 = 0; k0 < D; k0 += 16) {
-      const float4 av = ld4(ar + k0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = mma16(acc[i], av, col4(S + (k0 + 4 * q) * D + col(i), D));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s1[row(e) * LD + col(i)] = rec[R_UT + row(e) * D + col(i)] - acc[i][e];
+  for (int x = 0; x < 2; ++x) {
+    const int e = 4 * (tid + 512 * x);
+    *reinterpret_cast<float4 *>(sM + (e >> 6) * LS + (e & 63)) = vm[x];
   }
-  // dU = P^T dO + K_dec dS_next  -> s2
-  clear();
-  {
-    for (int k0 = 16 * tm; k0 < C; k0 += 16) {
-      const float4 av = col4(rec + R_P + (k0 + 4 * q) * C + 16 * tm + r, C);
+  if (tid < C) sBeta[tid] = tid < Tc ? bt : 0.f;
+  sGa[tid] = ga;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = mma16(acc[i], av, col4(s3 + (k0 + 4 * q) * LD + col(i), LD));
-    }
-    const float *ar = rec + R_KD + (16 * tm + r) * D + 4 * q;
-#pragma unroll 2
-    for (int k0 = 0; k0 < D; k0 += 16) {
-      const float4 av = ld4(ar + k0);
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = mma16(acc[i], av, col4(dSn + (k0 + 4 * q) * D + col(i), D));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s2[row(e) * LD + col(i)] = acc[i][e];
-  }
-  // dQ~ = dO S^T: dq += dQ~ e^G, dG += dQ~ * Q~
-  clear();
-  {
-    const float *ar = s3 + (16 * tm + r) * LD + 4 * q;
-#pragma unroll 2
-    for (int k0 = 0; k0 < D; k0 += 16) {
-      const float4 av = ld4(ar + k0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = mma16(acc[i], av, ld4(S + col(i) * D + k0 + 4 * q));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float eg = exp2_fast(Gr[i][e]);
-        DQ[i][e] += acc[i][e] * eg;
-        DG[i][e] += acc[i][e] * qr[i][e] * eg;
-      }
-  }
-  __syncthreads();   // U (s1) and dU (s2) complete
+    for (int e = 0; e < 4; ++e)
+      if (row(e) >= Tc) { kr[i][e] = 0.f; qr[i][e] = 0.f; }
+  lds_barrier();
 
   // dP = Lower(dO U^T)  -> sP
   {
@@ -584,64 +643,100 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) sP[row(e) * LS + col(i)] = col(i) <= row(e) ? p[i][e] : 0.f;
   }
-  // dK_dec = U dS_next^T: dk += dK_dec e^{Gam - G}; keep dK_dec * K_dec
-  clear();
-  {
-    const float *ar = s1 + (16 * tm + r) * LD + 4 * q;
-#pragma unroll 2
-    for (int k0 = 0; k0 < D; k0 += 16) {
-      const float4 av = ld4(ar + k0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = mma16(acc[i], av, ld4(dSn + col(i) * D + k0 + 4 * q));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float f = exp2_fast(Gam[i] - Gr[i][e]);
-        DK[i][e] += acc[i][e] * f;
-        KT[i][e] = acc[i][e] * kr[i][e] * f;
-      }
-  }
-  __syncthreads();   // dO (s3) and U (s1) no longer read
 
-  // dW = -dU S^T -> s3;  k e^G -> s1
-  clear();
+  // One pass over the chunk's state S and state gradient dS_next, both as transposed
+  // right operands (B(k, n) = X[n][k], the lane's four rows of X loaded one 16-long block
+  // ahead of their MFMAs):  dQ~ = dO S^T,  dW = -dU S^T,  dK_dec = U dS_next^T,  and
+  // dD = rowsum(dS_next * S) from the same fragments (waves with tm = 0 cover all rows).
+  f32x4 aq[4], aw[4], ak[4];
+  float dd[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { aq[i] = zero4(); aw[i] = zero4(); ak[i] = zero4(); }
   {
-    const float *ar = s2 + (16 * tm + r) * LD + 4 * q;
+    auto load_bt = [&](float4 (&bt4)[4], const float *X, int kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bt4[i] = ld4(X + col(i) * D + 16 * kb + 4 * q);
+    };
+    float4 sc[4], sn[4], dc[4], dn[4];
+    load_bt(sc, S, 0);
+    load_bt(dc, dSn, 0);
+    const float *ao = s3 + (16 * tm + r) * LD + 4 * q, *adu = s2 + (16 * tm + r) * LD + 4 * q;
+    const float *au = s1 + (16 * tm + r) * LD + 4 * q;
 #pragma unroll 2
-    for (int k0 = 0; k0 < D; k0 += 16) {
-      const float4 av = ld4(ar + k0);
+    for (int kb = 0; kb < 8; ++kb) {
+      load_bt(sn, S, min(kb + 1, 7));
+      load_bt(dn, dSn, min(kb + 1, 7));
+      const float4 xo = ld4(ao + 16 * kb), xdu = ld4(adu + 16 * kb), xu = ld4(au + 16 * kb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] = mma16(acc[i], av, ld4(S + col(i) * D + k0 + 4 * q));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s3[row(e) * LD + col(i)] = -acc[i][e];
-        s1[row(e) * LD + col(i)] = kr[i][e] * exp2_fast(Gr[i][e]);
+      for (int i = 0; i < 4; ++i) {
+        aq[i] = mma16(aq[i], xo, sc[i]);
+        aw[i] = mma16(aw[i], xdu, sc[i]);
+        ak[i] = mma16(ak[i], xu, dc[i]);
+        dd[i] += sc[i].x * dc[i].x + sc[i].y * dc[i].y + sc[i].z * dc[i].z + sc[i].w * dc[i].w;
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { sc[i] = sn[i]; dc[i] = dn[i]; }
+    }
   }
-  __syncthreads();
+  if (tm == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float x = dd[i];
+      x += __shfl_xor(x, 16);
+      x += __shfl_xor(x, 32);
+      if (q == 0) sdD[col(i)] = x;
+    }
+  }
+  // dq += dQ~ e^G, dG += dQ~ * Q~;  dk += dK_dec e^{Gam - G}, keep dK_dec * K_dec
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float eg = exp2_fast(Gr[i][e]), f = exp2_fast(Gam[i] - Gr[i][e]);
+      DQ[i][e] += aq[i][e] * eg;
+      DG[i][e] += aq[i][e] * qr[i][e] * eg;
+      DK[i][e] += ak[i][e] * f;
+      KT[i][e] = ak[i][e] * kr[i][e] * f;
+    }
+  lds_barrier();   // dO (s3) and U (s1) no longer read
 
-  // dT = dU v^T + dW (k e^G)^T -> sT (lower, with the diagonal)
+  // dW -> s3;  k e^G -> s1
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      s3[row(e) * LD + col(i)] = -aw[i][e];
+      s1[row(e) * LD + col(i)] = kr[i][e] * exp2_fast(Gr[i][e]);
+    }
+  lds_barrier();
+
+  // dT = dU v^T + dW (k e^G)^T -> sT (lower, with the diagonal); v rows one block ahead
   {
     f32x4 p[2] = {zero4(), zero4()};
     const float *ar = s2 + (16 * tm + r) * LD + 4 * q;
-    const float *aw = s3 + (16 * tm + r) * LD + 4 * q;
-#pragma unroll 2
-    for (int k0 = 0; k0 < D; k0 += 16) {
-      const float4 av = ld4(ar + k0), aw4 = ld4(aw + k0);
+    const float *aw4p = s3 + (16 * tm + r) * LD + 4 * q;
+    auto load_v = [&](float4 (&v4)[2], int kb) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int j = col(i);
+        v4[i] = load4<BF16>(a.v, tok_off(a, b, h, t0 + min(j, Tc - 1)) + 16 * kb + 4 * q);
+        if (j >= Tc) v4[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    };
+    float4 vc[2], vn[2];
+    load_v(vc, 0);
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+      load_v(vn, min(kb + 1, 7));
+      const float4 av = ld4(ar + 16 * kb), aw4 = ld4(aw4p + 16 * kb);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         if (tn0 + 2 * i <= tm) {
-          const int j = col(i);
-          float4 vv = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (j < Tc) vv = load4<BF16>(a.v, tok_off(a, b, h, t0 + j) + k0 + 4 * q);
-          p[i] = mma16(p[i], av, vv);
-          p[i] = mma16(p[i], aw4, ld4(s1 + j * LD + k0 + 4 * q));
+          p[i] = mma16(p[i], av, vc[i]);
+          p[i] = mma16(p[i], aw4, ld4(s1 + col(i) * LD + 16 * kb + 4 * q));
         }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) vc[i] = vn[i];
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -654,7 +749,7 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) { av_acc[i] = zero4(); aw_acc[i] = zero4(); }
     for (int k0 = 16 * tm; k0 < C; k0 += 16) {   // M[t][j] = 0 for t < j
-      const float4 am = col4(rec + R_M + (k0 + 4 * q) * C + 16 * tm + r, C);
+      const float4 am = col4(sM + (k0 + 4 * q) * LS + 16 * tm + r, LS);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         av_acc[i] = mma16(av_acc[i], am, col4(s2 + (k0 + 4 * q) * LD + col(i), LD));
@@ -674,27 +769,28 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
       }
     }
   }
-  __syncthreads();   // dT complete
+  lds_barrier();   // dT complete; k e^G (s1) no longer read
 
   // dbeta_j, first part: sum_t dT[t][j] M[t][j]; then dT -> dT diag(beta) in place
   {
     const int j = tid >> 3, part = tid & 7;
-    float s = 0.f;
+    float sum = 0.f;
     const float bj = sBeta[j];
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const int t = 8 * part + x;
       const float v = sT[t * LS + j];
-      s += v * rec[R_M + t * C + j];
+      sum += v * sM[t * LS + j];
       sT[t * LS + j] = v * bj;
     }
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    if (part == 0) sB1[j] = s;
+    sum += __shfl_xor(sum, 1);
+    sum += __shfl_xor(sum, 2);
+    sum += __shfl_xor(sum, 4);
+    if (part == 0) sB1[j] = sum;
   }
-  __syncthreads();
-  // Y = dM M^T -> sY (only blocks on and below the diagonal are used)
+  lds_barrier();
+  // Y = dM M^T -> s1 (row stride LS; only blocks on and below the diagonal are used)
+  float *sYm = s1;
   {
     f32x4 p[2] = {zero4(), zero4()};
     const float *ar = sT + (16 * tm + r) * LS + 4 * q;
@@ -702,22 +798,27 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
       const float4 av = ld4(ar + k0);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (tn0 + 2 * i <= tm) p[i] = mma16(p[i], av, ld4(rec + R_M + col(i) * C + k0 + 4 * q));
+        if (tn0 + 2 * i <= tm) p[i] = mma16(p[i], av, ld4(sM + col(i) * LS + k0 + 4 * q));
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sY[row(e) * LS + col(i)] = p[i][e];
+      for (int e = 0; e < 4; ++e) sYm[row(e) * LS + col(i)] = p[i][e];
   }
-  __syncthreads();
+  lds_barrier();
   // dA = -M^T Y (strictly lower): dKK = beta_t dA -> sT; dbeta_t += sum_j dA[t][j] KK[t][j]
   {
+    float kk[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kk[i][e] = rec[R_KK + row(e) * C + col(i)];
     f32x4 p[2] = {zero4(), zero4()};
     for (int k0 = 16 * tm; k0 < C; k0 += 16) {   // M[u][t] = 0 for u < t
-      const float4 am = col4(rec + R_M + (k0 + 4 * q) * C + 16 * tm + r, C);
+      const float4 am = col4(sM + (k0 + 4 * q) * LS + 16 * tm + r, LS);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (tn0 + 2 * i <= tm) p[i] = mma16(p[i], am, col4(sY + (k0 + 4 * q) * LS + col(i), LS));
+        if (tn0 + 2 * i <= tm) p[i] = mma16(p[i], am, col4(sYm + (k0 + 4 * q) * LS + col(i), LS));
     }
     float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -727,41 +828,42 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
         const int t = row(e), j = col(i);
         const float da = j < t ? -p[i][e] : 0.f;
         sT[t * LS + j] = sBeta[t] * da;
-        part[e] += da * rec[R_KK + t * C + j];
+        part[e] += da * kk[i][e];
       }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      float s = part[e];
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      s += __shfl_xor(s, 4);
-      s += __shfl_xor(s, 8);
-      if (r == 0) sB2[tn0][row(e)] = s;
+      float x = part[e];
+      x += __shfl_xor(x, 1);
+      x += __shfl_xor(x, 2);
+      x += __shfl_xor(x, 4);
+      x += __shfl_xor(x, 8);
+      if (r == 0) sB2[tn0][row(e)] = x;
     }
   }
+  lds_barrier();   // Y (s1) no longer read
   // KL -> s1, KR -> s2, QR -> s3 (block start of each row's own 16-token block)
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float ga = sGa[tm * D + col(i)], G = Gr[i][e];
-      const float up = exp2_fast(G - ga), dn = exp2_fast(ga - G);
+      const float g0 = sGa[tm * D + col(i)], G = Gr[i][e];
+      const float up = exp2_fast(G - g0), dn = exp2_fast(g0 - G);
       s1[row(e) * LD + col(i)] = kr[i][e] * dn;
       s2[row(e) * LD + col(i)] = kr[i][e] * up;
       s3[row(e) * LD + col(i)] = qr[i][e] * up;
     }
-  __syncthreads();
+  lds_barrier();
 
   // pairwise terms, rows t (j in blocks bb <= t's block):
   //   sum_j dKK[t][j] e^{G_t-G_j} k_j = sum_bb e^{G_t - G_R(bb)} (dKK[t, bb] KL[bb])
   for (int bb = 0; bb <= tm; ++bb) {
     f32x4 x[4], y[4];
-    const float4 ak = ld4(sT + (16 * tm + r) * LS + 16 * bb + 4 * q);
+    const float4 akk = ld4(sT + (16 * tm + r) * LS + 16 * bb + 4 * q);
     const float4 ap = ld4(sP + (16 * tm + r) * LS + 16 * bb + 4 * q);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float4 bl = col4(s1 + (16 * bb + 4 * q) * LD + col(i), LD);
-      x[i] = mma16(zero4(), ak, bl);
+      x[i] = mma16(zero4(), akk, bl);
       y[i] = mma16(zero4(), ap, bl);
     }
 #pragma unroll
@@ -781,11 +883,11 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
   //   sum_t dKK[t][j] e^{G_t-G_j} k_t = sum_aa e^{G_R(aa) - G_j} (dKK[aa, j]^T KR[aa]), same for dP, q
   for (int aa = tm; aa < 4; ++aa) {
     f32x4 x[4];
-    const float4 ak = col4(sT + (16 * aa + 4 * q) * LS + 16 * tm + r, LS);
+    const float4 akk = col4(sT + (16 * aa + 4 * q) * LS + 16 * tm + r, LS);
     const float4 ap = col4(sP + (16 * aa + 4 * q) * LS + 16 * tm + r, LS);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x[i] = mma16(zero4(), ak, col4(s2 + (16 * aa + 4 * q) * LD + col(i), LD));
+      x[i] = mma16(zero4(), akk, col4(s2 + (16 * aa + 4 * q) * LD + col(i), LD));
       x[i] = mma16(x[i], ap, col4(s3 + (16 * aa + 4 * q) * LD + col(i), LD));
     }
 #pragma unroll
@@ -799,7 +901,14 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
       }
     }
   }
-  __syncthreads();   // s1, s2 free
+  // decays of the dg scan, loaded ahead: thread (channel si, quarter sp) owns tokens
+  // 16 sp .. 16 sp + 15 of channel si
+  const int si = tid & 127, sp = tid >> 7;
+  float gq[16];
+#pragma unroll
+  for (int x = 0; x < 16; ++x) gq[x] = a.g[tok_off(a, b, h, t0 + min(16 * sp + x, Tc - 1)) + si];
+  const float Dsi = rec[R_D + si];
+  lds_barrier();   // s1, s2, sP free
 
   // outputs dq, dk; dG - dK_dec*K_dec -> s1, dK_dec*K_dec -> s2
 #pragma unroll
@@ -816,23 +925,40 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
       s2[t * LD + col(i)] = KT[i][e];
     }
   }
-  __syncthreads();
-  if (tid < D) {
-    // dGam = sum_t dK_dec*K_dec + dD e^{Gam};  dg_u = mask_u (sum_{t >= u} dG_t + dGam)
-    const int i = tid;
-    float s = sdD[i] * rec[R_D + i];
-    for (int t = 0; t < C; ++t) s += s2[t * LD + i];
-    for (int u = C - 1; u >= 0; --u) {
-      s += s1[u * LD + i];
+  if (tid < C) {
+    const int t = tid;
+    if (t < Tc) a.dbeta[(static_cast<size_t>(b) * a.T + t0 + t) * a.H + h] = sB1[t] + sB2[0][t] + sB2[1][t];
+  }
+  lds_barrier();
+  // dg_u = mask_u (sum_{t >= u} dG_t + dGam),  dGam = sum_t dK_dec*K_dec + dD e^{Gam}:
+  // quarter sums, then each quarter's suffix scan from its offset
+  {
+    float ps = 0.f, ks = 0.f;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) {
+      ps += s1[(16 * sp + x) * LD + si];
+      ks += s2[(16 * sp + x) * LD + si];
+    }
+    sP[sp * D + si] = ps;
+    sP[4 * D + sp * D + si] = ks;
+  }
+  lds_barrier();
+  {
+    float off = sdD[si] * Dsi;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      off += sP[4 * D + p * D + si];
+      if (p > sp) off += sP[p * D + si];
+    }
+#pragma unroll
+    for (int x = 15; x >= 0; --x) {
+      const int u = 16 * sp + x;
+      off += s1[u * LD + si];
       if (u < Tc) {
-        const size_t o = tok_off(a, b, h, t0 + u) + i;
-        const float g = a.g[o];
-        a.dg[o] = (g >= kFloor && g <= 0.f) ? s : 0.f;
+        const float g = gq[x];
+        a.dg[tok_off(a, b, h, t0 + u) + si] = (g >= kFloor && g <= 0.f) ? off : 0.f;
       }
     }
-  } else if (tid >= 256 && tid < 256 + C) {
-    const int t = tid - 256;
-    if (t < Tc) a.dbeta[(static_cast<size_t>(b) * a.T + t0 + t) * a.H + h] = sB1[t] + sB2[0][t] + sB2[1][t];
   }
 }
 
@@ -840,7 +966,7 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
 
 size_t backward_workspace_bytes(int B, int T, int H) {
   const size_t nc = T > 0 ? (static_cast<size_t>(T) + C - 1) / C : 0;
-  return static_cast<size_t>(B) * H * nc * (static_cast<size_t>(REC) + 2 * D * D) * sizeof(float);
+  return static_cast<size_t>(B) * H * nc * (static_cast<size_t>(REC) + 2 * D * D + C * D) * sizeof(float);
 }
 
 hipError_t launch_backward(const kda_backward_desc &d, hipStream_t s) {
@@ -855,6 +981,7 @@ hipError_t launch_backward(const kda_backward_desc &d, hipStream_t s) {
   a.rec = ws;
   a.sin = ws + nch * REC;
   a.dsa = a.sin + nch * D * D;
+  a.du = a.dsa + nch * D * D;
   const int BH = d.B * d.H;
   if (BH == 0) return hipSuccess;
   const bool bf16 = d.in_dtype == KDA_BF16;
