@@ -39,16 +39,18 @@ constexpr int LD = D + 4;     // LDS row stride of [C][D] tiles
 constexpr int LS = C + 4;     // LDS row stride of [C][C] tiles
 constexpr int LV = 20;        // LDS row stride of [*][16] column blocks
 
-// per-chunk record, floats
-constexpr int R_G = 0;              // [C][D] G in log2 units
-constexpr int R_KD = R_G + C * D;   // [C][D] K_dec
-constexpr int R_W = R_KD + C * D;   // [C][D] W
-constexpr int R_UT = R_W + C * D;   // [C][D] U~, replaced by U = U~ - W S in the state sweep
-constexpr int R_QT = R_UT + C * D;  // [C][D] Q~
-constexpr int R_P = R_QT + C * D;   // [C][C] P (zero above the diagonal)
-constexpr int R_M = R_P + C * C;    // [C][C] M (zero above the diagonal)
-constexpr int R_KK = R_M + C * C;   // [C][C] KK (zero on and above the diagonal)
-constexpr int R_D = R_KK + C * C;   // [D] e^{Gam}
+// per-chunk record, floats.  P and W are also kept transposed, where that costs the
+// chunk kernel nothing (its MFMA output fragments hold four consecutive rows).
+constexpr int R_G = 0;                // [C][D] G in log2 units
+constexpr int R_KD = R_G + C * D;     // [C][D] K_dec
+constexpr int R_W = R_KD + C * D;     // [C][D] W
+constexpr int R_WT = R_W + C * D;     // [D][C] W^T
+constexpr int R_UT = R_WT + C * D;    // [C][D] U~, replaced by U = U~ - W S in the state sweep
+constexpr int R_QT = R_UT + C * D;    // [C][D] Q~
+constexpr int R_PT = R_QT + C * D;    // [C][C] P^T (zero below the diagonal)
+constexpr int R_M = R_PT + C * C;     // [C][C] M (zero above the diagonal)
+constexpr int R_KK = R_M + C * C;     // [C][C] KK (zero on and above the diagonal)
+constexpr int R_D = R_KK + C * C;     // [D] e^{Gam}
 constexpr int REC = R_D + D;
 
 struct BwdArgs {
@@ -184,7 +186,7 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
   // zero tiles above the block diagonal of KK and P
   for (int e = tid; e < C * C; e += 512) {
     const int t = e >> 6, j = e & 63;
-    if ((j >> 4) > (t >> 4)) { rec[R_KK + e] = 0.f; rec[R_P + e] = 0.f; }
+    if ((j >> 4) > (t >> 4)) { rec[R_KK + t * C + j] = 0.f; rec[R_PT + j * C + t] = 0.f; }
   }
   lds_barrier();
 
@@ -203,12 +205,16 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
         if (ta != tb) av = mul4(av, ld4(dl + k0));
         acc = mma16(acc, av, ld4(br + k0));
       }
+      if (is_p) {   // P^T[j][t], the lane's four t contiguous
+        const int j = 16 * tb + r, t4 = 16 * ta + 4 * q;
+        *reinterpret_cast<float4 *>(rec + R_PT + j * C + t4) =
+            make_float4(j <= t4 ? acc[0] : 0.f, j <= t4 + 1 ? acc[1] : 0.f, j <= t4 + 2 ? acc[2] : 0.f,
+                        j <= t4 + 3 ? acc[3] : 0.f);
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int t = 16 * ta + 4 * q + e, j = 16 * tb + r;
-        if (is_p) {
-          rec[R_P + t * C + j] = j <= t ? acc[e] : 0.f;
-        } else {
+        if (!is_p) {
           const float v = j < t ? acc[e] : 0.f;
           rec[R_KK + t * C + j] = v;
           sA[t * LS + j] = sBeta[t] * v;
@@ -306,13 +312,17 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
     }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
+    const int n = 16 * (tn0 + 2 * i) + r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int t = 16 * tm + 4 * q + e, n = 16 * (tn0 + 2 * i) + r;
+      const int t = 16 * tm + 4 * q + e;
       rec[R_W + t * D + n] = accW[i][e];
       rec[R_UT + t * D + n] = accU[i][e];
     }
+    *reinterpret_cast<float4 *>(rec + R_WT + n * C + 16 * tm + 4 * q) =
+        make_float4(accW[i][0], accW[i][1], accW[i][2], accW[i][3]);
+  }
 }
 
 // (sequence, head) and 16-column block of a sweep workgroup.  The eight column blocks of
@@ -329,14 +339,19 @@ __device__ __forceinline__ bool sweep_unit(int BH, int &bh, int &cb) {
 // bwd_fwd: states entering every chunk, for 16 value columns of one (sequence, head)
 // ---------------------------------------------------------------------------
 // Each chunk step has two phases, U = U~ - W S (rows 16w.. of U) and S = D S + K_dec^T U
-// (state rows 16(w + 4 it)..); the record fragments of a phase are loaded one phase
-// ahead, for the next chunk, so their latency overlaps the other phase.
+// (state rows 16(w + 4 it)..).  The record fragments of a phase are loaded one phase
+// ahead, for the next chunk, so their latency overlaps the other phase.  S and U are
+// kept in LDS transposed ([column][row], double buffered), so that an MFMA operand is
+// one 16-byte read and a step needs two barriers.
+constexpr int LT = D + 4;   // row stride of a transposed [16][D] block
+constexpr int LU = C + 4;   // row stride of a transposed [16][C] block
+
 struct FwdA { float4 w[8]; float ut[4]; };
-struct FwdB { float kd[2][4][4]; float d[2][4]; };
+struct FwdB { float4 kd[2][4]; float4 d[2]; };
 
 __global__ __launch_bounds__(256) void bwd_fwd(BwdArgs a) {
-  __shared__ __align__(16) float sS[D * LV];
-  __shared__ __align__(16) float sU[C * LV];
+  __shared__ __align__(16) float sSt[2][16 * LT];
+  __shared__ __align__(16) float sUt[2][16 * LU];
   int bh, cb;
   if (!sweep_unit(a.B * a.H, bh, cb)) return;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, q = lane >> 4;
@@ -356,83 +371,93 @@ __global__ __launch_bounds__(256) void bwd_fwd(BwdArgs a) {
     for (int it = 0; it < 2; ++it) {
       const int ib = 16 * (w + 4 * it);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x.kd[it][kb][e] = rec[R_KD + (16 * kb + 4 * q + e) * D + ib + r];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x.d[it][e] = rec[R_D + ib + 4 * q + e];
+      for (int kb = 0; kb < 4; ++kb) x.kd[it][kb] = col4(rec + R_KD + (16 * kb + 4 * q) * D + ib + r, D);
+      x.d[it] = ld4(rec + R_D + ib + 4 * q);
     }
   };
   // state rows 16(w + 4 it) + 4q + e, column c0 + r
   f32x4 S[2];
 #pragma unroll
-  for (int it = 0; it < 2; ++it)
+  for (int it = 0; it < 2; ++it) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * (w + 4 * it) + 4 * q + e;
       S[it][e] = a.S0 ? a.S0[(static_cast<size_t>(bh) * D + i) * D + c0 + r] : 0.f;
-      sS[i * LV + r] = S[it][e];
     }
+    *reinterpret_cast<float4 *>(&sSt[0][r * LT + 16 * (w + 4 * it) + 4 * q]) =
+        make_float4(S[it][0], S[it][1], S[it][2], S[it][3]);
+  }
   FwdA A;
   FwdB Bf;
   loadA(A, 0);
   loadB(Bf, 0);
   __syncthreads();
   for (int c = 0; c < a.NC; ++c) {
-    const int cn = min(c + 1, a.NC - 1);   // the last step reloads its own chunk
+    const int p = c & 1, cn = min(c + 1, a.NC - 1);   // the last step reloads its own chunk
+    float *rec = recs + static_cast<size_t>(c) * REC;
     float *sin = a.sin + (static_cast<size_t>(bh) * a.NC + c) * D * D;
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sin[(16 * (w + 4 * it) + 4 * q + e) * D + c0 + r] = S[it][e];
-    // U = U~ - W S, rows 16w..
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) acc = mma16(acc, A.w[kb], col4(sS + (16 * kb + 4 * q) * LV + r, LV));
-    float *rec = recs + static_cast<size_t>(c) * REC;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {   // U replaces U~ (its columns are this workgroup's alone)
-      const int t = 16 * w + 4 * q + e;
-      const float u = A.ut[e] - acc[e];
-      sU[t * LV + r] = u;
-      rec[R_UT + t * D + c0 + r] = u;
+    for (int x = 0; x < 2; ++x) {   // the entering state, rows of 16 columns from its LDS copy
+      const int idx = tid + 256 * x, i = idx >> 2, c4 = (idx & 3) * 4;
+      const float *src = &sSt[p][c4 * LT + i];
+      *reinterpret_cast<float4 *>(sin + i * D + c0 + c4) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
     }
+    // U = U~ - W S, rows 16w.. (two accumulation chains)
+    const float *bs = &sSt[p][r * LT + 4 * q];
+    f32x4 u0 = zero4(), u1 = zero4();
+#pragma unroll
+    for (int kb = 0; kb < 8; kb += 2) {
+      u0 = mma16(u0, A.w[kb], ld4(bs + 16 * kb));
+      u1 = mma16(u1, A.w[kb + 1], ld4(bs + 16 * kb + 16));
+    }
+    float u[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = A.ut[e] - (u0[e] + u1[e]);
+    *reinterpret_cast<float4 *>(&sUt[p][r * LU + 16 * w + 4 * q]) = make_float4(u[0], u[1], u[2], u[3]);
     loadA(A, cn);
     lds_barrier();
+    {   // U replaces U~ (its columns are this workgroup's alone), rows from the LDS copy
+      const int t = tid >> 2, c4 = (tid & 3) * 4;
+      const float *src = &sUt[p][c4 * LU + t];
+      *reinterpret_cast<float4 *>(rec + R_UT + t * D + c0 + c4) = make_float4(src[0], src[LU], src[2 * LU], src[3 * LU]);
+    }
     // S = D S + K_dec^T U
+    const float *bu = &sUt[p][r * LU + 4 * q];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-      f32x4 s;
+      f32x4 s0, s1 = zero4();
+      s0[0] = Bf.d[it].x * S[it][0];
+      s0[1] = Bf.d[it].y * S[it][1];
+      s0[2] = Bf.d[it].z * S[it][2];
+      s0[3] = Bf.d[it].w * S[it][3];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s[e] = Bf.d[it][e] * S[it][e];
+      for (int kb = 0; kb < 4; kb += 2) {
+        s0 = mma16(s0, Bf.kd[it][kb], ld4(bu + 16 * kb));
+        s1 = mma16(s1, Bf.kd[it][kb + 1], ld4(bu + 16 * kb + 16));
+      }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        s = mma16(s, make_float4(Bf.kd[it][kb][0], Bf.kd[it][kb][1], Bf.kd[it][kb][2], Bf.kd[it][kb][3]),
-                  col4(sU + (16 * kb + 4 * q) * LV + r, LV));
-      S[it] = s;
+      for (int e = 0; e < 4; ++e) S[it][e] = s0[e] + s1[e];
+      *reinterpret_cast<float4 *>(&sSt[p ^ 1][r * LT + 16 * (w + 4 * it) + 4 * q]) =
+          make_float4(S[it][0], S[it][1], S[it][2], S[it][3]);
     }
     loadB(Bf, cn);
-    lds_barrier();
-#pragma unroll
-    for (int it = 0; it < 2; ++it)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sS[(16 * (w + 4 * it) + 4 * q + e) * LV + r] = S[it][e];
     lds_barrier();
   }
 }
 
 // ---------------------------------------------------------------------------
-// bwd_rev: dS after every chunk (reverse order) and dS0
+// bwd_rev: dS after every chunk (reverse order), dU, and dS0
 // ---------------------------------------------------------------------------
 // Phases dU = P^T dO + K_dec dS (rows 16w..) and dS = D dS + Q~^T dO - W^T dU, with the
-// record fragments and the dO block of the next (earlier) chunk loaded one phase ahead.
-struct RevA { float p[4][4]; float4 kd[8]; };
-struct RevB { float qt[2][4][4]; float wt[2][4][4]; float d[2][4]; };
+// record fragments of the next (earlier) chunk loaded one phase ahead and its dO block
+// one step ahead.  dS, dO and dU blocks are kept in LDS transposed and double buffered.
+struct RevA { float4 p[4]; float4 kd[8]; };
+struct RevB { float4 qt[2][4]; float4 wt[2][4]; float4 d[2]; };
 
 __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
-  __shared__ __align__(16) float sdS[D * LV];
-  __shared__ __align__(16) float sdO[C * LV];
-  __shared__ __align__(16) float sdU[C * LV];
+  __shared__ __align__(16) float sdSt[2][16 * LT];
+  __shared__ __align__(16) float sdOt[2][16 * LU];
+  __shared__ __align__(16) float sdUt[2][16 * LU];
   int bh, cb;
   if (!sweep_unit(a.B * a.H, bh, cb)) return;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, q = lane >> 4;
@@ -443,8 +468,7 @@ __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
     const float *rec = recs + static_cast<size_t>(c) * REC;
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)   // P^T[t'][t] (zero for t < t')
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x.p[kb][e] = rec[R_P + (16 * kb + 4 * q + e) * C + 16 * w + r];
+      x.p[kb] = ld4(rec + R_PT + (16 * w + r) * C + 16 * kb + 4 * q);
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) x.kd[kb] = ld4(rec + R_KD + (16 * w + r) * D + 16 * kb + 4 * q);
   };
@@ -454,17 +478,15 @@ __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
     for (int it = 0; it < 2; ++it) {
       const int ib = 16 * (w + 4 * it);
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x.qt[it][kb][e] = rec[R_QT + (16 * kb + 4 * q + e) * D + ib + r];
-          x.wt[it][kb][e] = rec[R_W + (16 * kb + 4 * q + e) * D + ib + r];
-        }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) x.d[it][e] = rec[R_D + ib + 4 * q + e];
+      for (int kb = 0; kb < 4; ++kb) {
+        x.qt[it][kb] = col4(rec + R_QT + (16 * kb + 4 * q) * D + ib + r, D);
+        x.wt[it][kb] = ld4(rec + R_WT + (ib + r) * C + 16 * kb + 4 * q);
+      }
+      x.d[it] = ld4(rec + R_D + ib + 4 * q);
     }
   };
-  // one float4 of the chunk's dO block [64][16] per thread (rows past the end read 0)
+  // one float4 of a chunk's dO block [64][16] per thread (rows past the end read 0),
+  // stored transposed
   const int ot = tid >> 2, ox = (tid & 3) * 4;
   auto loadO = [&](int c) {
     const int t = c * C + ot;
@@ -472,68 +494,87 @@ __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
     if (t >= a.T) v = make_float4(0.f, 0.f, 0.f, 0.f);
     return v;
   };
+  auto storeO = [&](float *dst, float4 v) {
+    dst[(ox + 0) * LU + ot] = v.x;
+    dst[(ox + 1) * LU + ot] = v.y;
+    dst[(ox + 2) * LU + ot] = v.z;
+    dst[(ox + 3) * LU + ot] = v.w;
+  };
   f32x4 dS[2];
 #pragma unroll
-  for (int it = 0; it < 2; ++it)
+  for (int it = 0; it < 2; ++it) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * (w + 4 * it) + 4 * q + e;
       dS[it][e] = a.dSf ? a.dSf[(static_cast<size_t>(bh) * D + i) * D + c0 + r] : 0.f;
-      sdS[i * LV + r] = dS[it][e];
     }
+    *reinterpret_cast<float4 *>(&sdSt[0][r * LT + 16 * (w + 4 * it) + 4 * q]) =
+        make_float4(dS[it][0], dS[it][1], dS[it][2], dS[it][3]);
+  }
   if (a.NC > 0) {
     RevA A;
     RevB Bf;
-    float4 ov = loadO(a.NC - 1);
+    storeO(sdOt[0], loadO(a.NC - 1));
     loadA(A, a.NC - 1);
     loadB(Bf, a.NC - 1);
-    for (int c = a.NC - 1; c >= 0; --c) {
+    __syncthreads();
+    for (int c = a.NC - 1, p = 0; c >= 0; --c, p ^= 1) {
       const int cn = max(c - 1, 0);   // the last step reloads its own chunk
       float *dsa = a.dsa + (static_cast<size_t>(bh) * a.NC + c) * D * D;
 #pragma unroll
-      for (int it = 0; it < 2; ++it)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dsa[(16 * (w + 4 * it) + 4 * q + e) * D + c0 + r] = dS[it][e];
-      *reinterpret_cast<float4 *>(sdO + ot * LV + ox) = ov;
-      lds_barrier();
-      ov = loadO(cn);
-      // dU = P^T dO + K_dec dS, rows 16w..
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        acc = mma16(acc, make_float4(A.p[kb][0], A.p[kb][1], A.p[kb][2], A.p[kb][3]),
-                    col4(sdO + (16 * kb + 4 * q) * LV + r, LV));
-#pragma unroll
-      for (int kb = 0; kb < 8; ++kb) acc = mma16(acc, A.kd[kb], col4(sdS + (16 * kb + 4 * q) * LV + r, LV));
-      float *du = a.du + (static_cast<size_t>(bh) * a.NC + c) * C * D;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sdU[(16 * w + 4 * q + e) * LV + r] = acc[e];
-        du[(16 * w + 4 * q + e) * D + c0 + r] = acc[e];
+      for (int x = 0; x < 2; ++x) {   // dS after this chunk, rows of 16 columns from its LDS copy
+        const int idx = tid + 256 * x, i = idx >> 2, c4 = (idx & 3) * 4;
+        const float *src = &sdSt[p][c4 * LT + i];
+        *reinterpret_cast<float4 *>(dsa + i * D + c0 + c4) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
       }
+      const float4 ov = loadO(cn);
+      // dU = P^T dO + K_dec dS, rows 16w.. (two accumulation chains)
+      const float *bo = &sdOt[p][r * LU + 4 * q], *bs = &sdSt[p][r * LT + 4 * q];
+      f32x4 u0 = zero4(), u1 = zero4();
+#pragma unroll
+      for (int kb = 0; kb < 4; kb += 2) {
+        u0 = mma16(u0, A.p[kb], ld4(bo + 16 * kb));
+        u1 = mma16(u1, A.p[kb + 1], ld4(bo + 16 * kb + 16));
+      }
+#pragma unroll
+      for (int kb = 0; kb < 8; kb += 2) {
+        u0 = mma16(u0, A.kd[kb], ld4(bs + 16 * kb));
+        u1 = mma16(u1, A.kd[kb + 1], ld4(bs + 16 * kb + 16));
+      }
+      float uu[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) uu[e] = u0[e] + u1[e];
+      *reinterpret_cast<float4 *>(&sdUt[p][r * LU + 16 * w + 4 * q]) = make_float4(uu[0], uu[1], uu[2], uu[3]);
       loadA(A, cn);
       lds_barrier();
+      {   // dU rows from the LDS copy
+        float *du = a.du + (static_cast<size_t>(bh) * a.NC + c) * C * D;
+        const int t = tid >> 2, c4 = (tid & 3) * 4;
+        const float *src = &sdUt[p][c4 * LU + t];
+        *reinterpret_cast<float4 *>(du + t * D + c0 + c4) = make_float4(src[0], src[LU], src[2 * LU], src[3 * LU]);
+      }
       // dS = D dS + Q~^T dO - W^T dU
+      const float *bu = &sdUt[p][r * LU + 4 * q];
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
-        f32x4 s;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[e] = Bf.d[it][e] * dS[it][e];
+        f32x4 s0, s1 = zero4();
+        s0[0] = Bf.d[it].x * dS[it][0];
+        s0[1] = Bf.d[it].y * dS[it][1];
+        s0[2] = Bf.d[it].z * dS[it][2];
+        s0[3] = Bf.d[it].w * dS[it][3];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          const float4 qv = make_float4(Bf.qt[it][kb][0], Bf.qt[it][kb][1], Bf.qt[it][kb][2], Bf.qt[it][kb][3]);
-          const float4 wv = make_float4(Bf.wt[it][kb][0], Bf.wt[it][kb][1], Bf.wt[it][kb][2], Bf.wt[it][kb][3]);
-          s = mma16(s, qv, col4(sdO + (16 * kb + 4 * q) * LV + r, LV));
-          s = mma16(s, wv, neg4(col4(sdU + (16 * kb + 4 * q) * LV + r, LV)));
+          s0 = mma16(s0, Bf.qt[it][kb], ld4(bo + 16 * kb));
+          s1 = mma16(s1, Bf.wt[it][kb], neg4(ld4(bu + 16 * kb)));
         }
-        dS[it] = s;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dS[it][e] = s0[e] + s1[e];
+        *reinterpret_cast<float4 *>(&sdSt[p ^ 1][r * LT + 16 * (w + 4 * it) + 4 * q]) =
+            make_float4(dS[it][0], dS[it][1], dS[it][2], dS[it][3]);
       }
+      storeO(sdOt[p ^ 1], ov);
       loadB(Bf, cn);
       lds_barrier();
-#pragma unroll
-      for (int it = 0; it < 2; ++it)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sdS[(16 * (w + 4 * it) + 4 * q + e) * LV + r] = dS[it][e];
     }
   }
   if (a.dS0)
