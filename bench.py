@@ -1,13 +1,14 @@
 """Benchmark of the KDA hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
 
 Headline (`value`): chunkwise prefill tokens/s on the prefill workload B=4, H=16,
 T=8192, d=128, chunk 64, bf16 q/k/v/gate, fp32 g/beta/state, S0 ~ N(0, 0.01), with the
 fused per-head RMSNorm and sigmoid gate, fp32 output.  One step = one prefill call over
 the whole batch with inputs resident in HBM.  The same run also times the decode
 workload (256 sequences x 16 heads, fp32 states, one kernel per step) and reports its
-sequence-steps/s.
+sequence-steps/s, decode over a pool of state slots, and the backward pass of the same
+prefill (gradients of the raw outputs, fp32 MFMA) against the fp32 matrix peak.
 
 Prints one JSON line with a `roofline` object for the prefill kernel (algorithmic bytes
 over measured duration against 8 TB/s) and a `cpu_baseline` object (the fp64 C oracle
@@ -29,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense BF16/FP16 MFMA, TFLOP/s
+FP32_PEAK_TFLOPS = 157.3       # MI355X dense FP32 MFMA, TFLOP/s
 D = 128
 
 
@@ -43,6 +45,20 @@ def prefill_alg_flops(B, T, H, chunk=64):
     """Chunkwise flops per token-head: 6 d^2 (state products) + C (3 d_k + 2 d_v)
     (intra-chunk products, triangles counted once)."""
     return B * T * H * (6 * D * D + chunk * (3 * D + 2 * D))
+
+
+def backward_alg_flops(B, T, H, chunk=64):
+    """Multiply-adds the chunkwise backward needs per 64-token chunk and head, x2, counting a
+    triangular factor at half: chunk quantities KK, P, W, U~ (4 C^2/2 d); state sweep W S and
+    K_dec^T U (2 C d^2); gradient sweep P^T dO (C^2/2 d), K_dec dS, Q~^T dO, W^T dU (3 C d^2);
+    per-chunk dP (C^2/2 d), dO S^T, dU S^T, U dS^T (3 C d^2), dT (2 C^2/2 d), T^T dU, T^T dW
+    (2 C^2/2 d), dM M^T and M^T Y (2 C^3/2), and the four pairwise products (4 C^2/2 d)."""
+    C, d = chunk, D
+    n = B * H * ((T + C - 1) // C)
+    macs = (4 * C * C // 2 * d + 2 * C * d * d + C * C // 2 * d + 3 * C * d * d + C * C // 2 * d
+            + 3 * C * d * d + 2 * C * C // 2 * d + 2 * C * C // 2 * d + 2 * C ** 3 // 2
+            + 4 * C * C // 2 * d)
+    return 2 * macs * n
 
 
 def decode_alg_bytes(N, H):
@@ -99,6 +115,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--v-split", type=int, default=0)
     ap.add_argument("--n-segments", type=int, default=0)
     a = ap.parse_args()
@@ -288,6 +305,47 @@ def main():
                                           "GB_per_s": round(N * Hs * D * D * 4 / (wb_ms * 1e-3) / 1e9, 1)},
         }
         del pool, host
+
+    # ---------------- backward of the prefill (training) ----------------
+    if not a.no_backward:
+        from kda_inputs import make_output_grads
+        dO_np, dS_np = make_output_grads(B, T, H, D, seed=0)
+        dO, dSf = up(dO_np), up(dS_np)
+        del dO_np
+        grads = dict(dq=torch.empty((B, T, H, D), device=dev), dk=torch.empty((B, T, H, D), device=dev),
+                     dv=torch.empty((B, T, H, D), device=dev), dg=torch.empty((B, T, H, D), device=dev),
+                     dbeta=torch.empty((B, T, H), device=dev), dS0=torch.empty((B, H, D, D), device=dev))
+        bws = torch.empty(kda.kda_backward_workspace_size(q, k, v, g, beta, dO), dtype=torch.uint8,
+                          device=dev)
+
+        def bstep():
+            kda.kda_prefill_backward(q, k, v, g, beta, dO, S0=S0, dS_final=dSf, workspace=bws,
+                                     stream=stream, **grads)
+
+        for _ in range(3):
+            bstep()
+        torch.cuda.synchronize()
+        nb = 10
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(nb):
+            bstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / nb
+        bf = backward_alg_flops(B, T, H)
+        out["backward"] = {
+            "workload": "gradients of the raw-output prefill above (same q/k/v/g/beta/S0; "
+                        "dO ~ N(0,1), dS_T ~ N(0,0.01) fp32): dq, dk, dv, dg, dbeta, dS0 fp32",
+            "ms_per_call": round(bms, 3),
+            "tokens_per_s": round(B * T / (bms * 1e-3), 1),
+            "mfma": {"bound": "mfma", "alg_flops_per_launch": bf,
+                     "achieved": round(bf / (bms * 1e-3) / 1e12, 2), "peak": FP32_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(bf / (bms * 1e-3) / 1e12 / FP32_PEAK_TFLOPS, 4),
+                     "kernels": "bwd_prep, bwd_fwd, bwd_rev, bwd_grad; fp32 MFMA"},
+            "workspace_bytes": int(bws.numel()),
+        }
+        del grads, bws, dO, dSf
 
     # one copy kernel of known size (state checkpoint, 64 MiB each way) after the timed regions:
     # counter runs use it to calibrate FETCH_SIZE / WRITE_SIZE against known bytes

@@ -387,13 +387,17 @@ __global__ __launch_bounds__(256) void bwd_fwd(BwdArgs a) {
     *reinterpret_cast<float4 *>(&sSt[0][r * LT + 16 * (w + 4 * it) + 4 * q]) =
         make_float4(S[it][0], S[it][1], S[it][2], S[it][3]);
   }
-  FwdA A;
-  FwdB Bf;
-  loadA(A, 0);
-  loadB(Bf, 0);
+  // two register sets in fixed roles (even and odd chunks): a set is refilled with the
+  // chunk two steps ahead as soon as its phase has consumed it
+  FwdA A0, A1;
+  FwdB B0, B1;
+  loadA(A0, 0);
+  loadB(B0, 0);
+  loadA(A1, min(1, a.NC - 1));
+  loadB(B1, min(1, a.NC - 1));
   __syncthreads();
-  for (int c = 0; c < a.NC; ++c) {
-    const int p = c & 1, cn = min(c + 1, a.NC - 1);   // the last step reloads its own chunk
+  auto step = [&](FwdA &A, FwdB &Bf, int c) __attribute__((always_inline)) {
+    const int p = c & 1, cn = min(c + 2, a.NC - 1);   // the last steps reload a chunk of their own
     float *rec = recs + static_cast<size_t>(c) * REC;
     float *sin = a.sin + (static_cast<size_t>(bh) * a.NC + c) * D * D;
 #pragma unroll
@@ -442,7 +446,15 @@ __global__ __launch_bounds__(256) void bwd_fwd(BwdArgs a) {
     }
     loadB(Bf, cn);
     lds_barrier();
+  };
+  // both steps unconditional in the loop (an odd last chunk runs after it), so that the
+  // compiler's wait counts for the prefetched sets stay exact across the back edge
+  int c = 0;
+  for (; c + 1 < a.NC; c += 2) {
+    step(A0, B0, c);
+    step(A1, B1, c + 1);
   }
+  if (c < a.NC) step(A0, B0, c);
 }
 
 // ---------------------------------------------------------------------------
@@ -451,8 +463,10 @@ __global__ __launch_bounds__(256) void bwd_fwd(BwdArgs a) {
 // Phases dU = P^T dO + K_dec dS (rows 16w..) and dS = D dS + Q~^T dO - W^T dU, with the
 // record fragments of the next (earlier) chunk loaded one phase ahead and its dO block
 // one step ahead.  dS, dO and dU blocks are kept in LDS transposed and double buffered.
-struct RevA { float4 p[4]; float4 kd[8]; };
-struct RevB { float4 qt[2][4]; float4 wt[2][4]; float4 d[2]; };
+// (D rides with the phase-A fragments: loaded half a step earlier than the phase-B set,
+// its early use does not wait for that set)
+struct RevA { float4 p[4]; float4 kd[8]; float4 d[2]; };
+struct RevB { float4 qt[2][4]; float4 wt[2][4]; };
 
 __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
   __shared__ __align__(16) float sdSt[2][16 * LT];
@@ -471,6 +485,8 @@ __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
       x.p[kb] = ld4(rec + R_PT + (16 * w + r) * C + 16 * kb + 4 * q);
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) x.kd[kb] = ld4(rec + R_KD + (16 * w + r) * D + 16 * kb + 4 * q);
+#pragma unroll
+    for (int it = 0; it < 2; ++it) x.d[it] = ld4(rec + R_D + 16 * (w + 4 * it) + 4 * q);
   };
   auto loadB = [&](RevB &x, int c) {
     const float *rec = recs + static_cast<size_t>(c) * REC;
@@ -482,7 +498,6 @@ __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
         x.qt[it][kb] = col4(rec + R_QT + (16 * kb + 4 * q) * D + ib + r, D);
         x.wt[it][kb] = ld4(rec + R_WT + (ib + r) * C + 16 * kb + 4 * q);
       }
-      x.d[it] = ld4(rec + R_D + ib + 4 * q);
     }
   };
   // one float4 of a chunk's dO block [64][16] per thread (rows past the end read 0),
@@ -545,6 +560,7 @@ __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) uu[e] = u0[e] + u1[e];
       *reinterpret_cast<float4 *>(&sdUt[p][r * LU + 16 * w + 4 * q]) = make_float4(uu[0], uu[1], uu[2], uu[3]);
+      const float4 dcur[2] = {A.d[0], A.d[1]};
       loadA(A, cn);
       lds_barrier();
       {   // dU rows from the LDS copy
@@ -558,10 +574,10 @@ __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
 #pragma unroll
       for (int it = 0; it < 2; ++it) {
         f32x4 s0, s1 = zero4();
-        s0[0] = Bf.d[it].x * dS[it][0];
-        s0[1] = Bf.d[it].y * dS[it][1];
-        s0[2] = Bf.d[it].z * dS[it][2];
-        s0[3] = Bf.d[it].w * dS[it][3];
+        s0[0] = dcur[it].x * dS[it][0];
+        s0[1] = dcur[it].y * dS[it][1];
+        s0[2] = dcur[it].z * dS[it][2];
+        s0[3] = dcur[it].w * dS[it][3];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           s0 = mma16(s0, Bf.qt[it][kb], ld4(bo + 16 * kb));

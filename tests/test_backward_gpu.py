@@ -13,7 +13,8 @@ import pytest
 import torch
 
 import linear_attention_sequence_kda_amd as kda
-from kda_inputs import BF16, F32, make_output_grads, make_prefill, to_f64
+from kda_inputs import BF16, F32, make_output_grads, make_prefill, make_workload, to_f64
+from oracle import native
 from oracle.backward import backward
 from gpu_util import up, down, err_o, err_S, dev
 
@@ -28,7 +29,8 @@ def _say(*a):
     print(*a, flush=True, file=sys.stderr)
 
 
-def run_gpu(c, dO, dS, *, S0=True):
+def run_gpu_t(c, dO, dS, *, S0=True):
+    """Gradients as device tensors."""
     B, T, H = c.B, c.T, c.H
     nan = float("nan")
     out = {n: torch.full((B, T, H, 128), nan, device=dev()) for n in ("dq", "dk", "dv", "dg")}
@@ -37,7 +39,11 @@ def run_gpu(c, dO, dS, *, S0=True):
     kda.kda_prefill_backward(up(c.q), up(c.k), up(c.v), up(c.g), up(c.beta), up(dO),
                              S0=up(c.S0) if S0 else None, dS_final=up(dS), **out)
     torch.cuda.synchronize()
-    return {n: down(t) for n, t in out.items()}
+    return out
+
+
+def run_gpu(c, dO, dS, *, S0=True):
+    return {n: down(t) for n, t in run_gpu_t(c, dO, dS, S0=S0).items()}
 
 
 def run_oracle(c, dO, dS, *, S0=True):
@@ -111,3 +117,38 @@ def test_backward_empty_sequence():
                              dS0=dS0)
     torch.cuda.synchronize()
     assert torch.equal(dS0.cpu(), torch.from_numpy(dS))
+
+
+def test_backward_one_head_2k_of_the_prefill_workload():
+    """A whole head of the prefill workload's distributions over 2048 tokens (32 chunks),
+    every gradient against the oracle."""
+    c = make_workload("prefill_8k", seed=5, T=2048, B=1, H=1, in_dtype=BF16)
+    dO, dS = make_output_grads(1, 2048, 1, seed=5)
+    check(c, dO, dS, "prefill workload, one head, T=2048")
+
+
+def test_backward_full_size_sampled_dq():
+    """The full prefill workload (B=4, T=8192, H=16, S0): o_t = S_t^T q_t and S_t does not
+    depend on q_t, so dq_t = S_t dO_t exactly, with S_t the state after token t.  S_t from
+    the fp64 oracle over the prefix, at sampled (b, t, h) on chunk edges, inside chunks
+    and at the last token; every gradient finite."""
+    c = make_workload("prefill_8k", seed=0)
+    B, T, H = c.B, c.T, c.H
+    dO, dS = make_output_grads(B, T, H, seed=0)
+    _say(f"backward full size: B={B} T={T} H={H}")
+    got = run_gpu_t(c, dO, dS)
+    for n, t in got.items():
+        assert bool(torch.isfinite(t).all()), n
+    dq = got["dq"]
+    samples = [(0, 0, 0), (1, 63, 5), (2, 64, 11), (3, 4095, 15), (0, 8191, 7), (2, 5000, 3),
+               (3, 8191, 0), (1, 2047, 9)]
+    err = []
+    for b, t, h in samples:
+        sl = (slice(b, b + 1), slice(0, t + 1), slice(h, h + 1))
+        _, St, _ = native.prefill(c.q[sl], c.k[sl], c.v[sl], c.g[sl], c.beta[sl],
+                                  c.S0[b:b + 1, h:h + 1], bf16=True, want_o=False)
+        ref = St[0, 0] @ dO[b, t, h].astype(np.float64)
+        e = err_o(down(dq[b, t, h]), ref)
+        _say(f"  dq at (b={b}, t={t}, h={h}): err={e:.3e}")
+        err.append(e)
+    assert max(err) <= TOL
