@@ -83,6 +83,14 @@ __device__ __forceinline__ float4 mul4(float4 a, float4 b) {
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// Column-blocked layout of the per-chunk states, their gradients, U and dU: element
+// (row, col) of a [rows][D] matrix sits at (col / 16) [rows] [16] + (row, col % 16), so a
+// sweep workgroup's 16 columns are one contiguous block (whole-line stores) and a
+// 16-byte piece of a row stays contiguous for the per-chunk kernel.
+__device__ __forceinline__ int cblk(int row, int col, int rows) {
+  return (col >> 4) * rows * 16 + row * 16 + (col & 15);
+}
+
 // element offset of token t of chunk c in a [B,T,H,D] array
 __device__ __forceinline__ size_t tok_off(const BwdArgs &a, int b, int h, int t) {
   return (static_cast<size_t>(b) * a.T + t) * a.H * D + static_cast<size_t>(h) * D;
@@ -318,7 +326,7 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
     for (int e = 0; e < 4; ++e) {
       const int t = 16 * tm + 4 * q + e;
       rec[R_W + t * D + n] = accW[i][e];
-      rec[R_UT + t * D + n] = accU[i][e];
+      rec[R_UT + cblk(t, n, C)] = accU[i][e];
     }
     *reinterpret_cast<float4 *>(rec + R_WT + n * C + 16 * tm + 4 * q) =
         make_float4(accW[i][0], accW[i][1], accW[i][2], accW[i][3]);
@@ -338,171 +346,152 @@ __device__ __forceinline__ bool sweep_unit(int BH, int &bh, int &cb) {
 // ---------------------------------------------------------------------------
 // bwd_fwd: states entering every chunk, for 16 value columns of one (sequence, head)
 // ---------------------------------------------------------------------------
-// Each chunk step has two phases, U = U~ - W S (rows 16w.. of U) and S = D S + K_dec^T U
-// (state rows 16(w + 4 it)..).  The record fragments of a phase are loaded one phase
-// ahead, for the next chunk, so their latency overlaps the other phase.  S and U are
-// kept in LDS transposed ([column][row], double buffered), so that an MFMA operand is
-// one 16-byte read and a step needs two barriers.
+// Eight waves per unit.  Each chunk step has two phases: U = U~ - W S (wave w: rows
+// 16(w&3).. of U over half of the contraction, (w>>2)), then S = D S + K_dec^T U (wave w:
+// state rows 16w..).  The record fragments of a phase are loaded one step ahead, so their
+// latency overlaps the other phase; with 128 registers two units share a CU (16 waves).
+// S and the two partial sums of U are kept in LDS transposed ([column][row],
+// double buffered), so that an MFMA operand is one 16-byte read and a step needs two
+// barriers; state and U rows go to global memory as 16-byte stores from those copies.
 constexpr int LT = D + 4;   // row stride of a transposed [16][D] block
 constexpr int LU = C + 4;   // row stride of a transposed [16][C] block
 
-struct FwdA { float4 w[8]; float ut[4]; };
-struct FwdB { float4 kd[2][4]; float4 d[2]; };
+struct FwdA { float4 w[4]; float ut[4]; };
+struct FwdB { float4 kd[4]; float4 d; };
 
-__global__ __launch_bounds__(256) void bwd_fwd(BwdArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void bwd_fwd(BwdArgs a) {
   __shared__ __align__(16) float sSt[2][16 * LT];
-  __shared__ __align__(16) float sUt[2][16 * LU];
+  __shared__ __align__(16) float sUt[2][2][16 * LU];
   int bh, cb;
   if (!sweep_unit(a.B * a.H, bh, cb)) return;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, q = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ta = w & 3, kh = w >> 2;
   const int c0 = 16 * cb;
   float *recs = a.rec + static_cast<size_t>(bh) * a.NC * REC;
   auto loadA = [&](FwdA &x, int c) {
     const float *rec = recs + static_cast<size_t>(c) * REC;
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) x.w[kb] = ld4(rec + R_W + (16 * w + r) * D + 16 * kb + 4 * q);
+    for (int j = 0; j < 4; ++j) x.w[j] = ld4(rec + R_W + (16 * ta + r) * D + 16 * (4 * kh + j) + 4 * q);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x.ut[e] = rec[R_UT + (16 * w + 4 * q + e) * D + c0 + r];
+    for (int e = 0; e < 4; ++e) x.ut[e] = rec[R_UT + cblk(16 * ta + 4 * q + e, c0 + r, C)];
   };
   auto loadB = [&](FwdB &x, int c) {
     const float *rec = recs + static_cast<size_t>(c) * REC;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int ib = 16 * (w + 4 * it);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) x.kd[it][kb] = col4(rec + R_KD + (16 * kb + 4 * q) * D + ib + r, D);
-      x.d[it] = ld4(rec + R_D + ib + 4 * q);
-    }
+    for (int kb = 0; kb < 4; ++kb) x.kd[kb] = col4(rec + R_KD + (16 * kb + 4 * q) * D + 16 * w + r, D);
+    x.d = ld4(rec + R_D + 16 * w + 4 * q);
   };
-  // state rows 16(w + 4 it) + 4q + e, column c0 + r
-  f32x4 S[2];
+  // state rows 16w + 4q + e, column c0 + r
+  f32x4 S;
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * (w + 4 * it) + 4 * q + e;
-      S[it][e] = a.S0 ? a.S0[(static_cast<size_t>(bh) * D + i) * D + c0 + r] : 0.f;
-    }
-    *reinterpret_cast<float4 *>(&sSt[0][r * LT + 16 * (w + 4 * it) + 4 * q]) =
-        make_float4(S[it][0], S[it][1], S[it][2], S[it][3]);
-  }
-  // two register sets in fixed roles (even and odd chunks): a set is refilled with the
-  // chunk two steps ahead as soon as its phase has consumed it
-  FwdA A0, A1;
-  FwdB B0, B1;
-  loadA(A0, 0);
-  loadB(B0, 0);
-  loadA(A1, min(1, a.NC - 1));
-  loadB(B1, min(1, a.NC - 1));
+  for (int e = 0; e < 4; ++e)
+    S[e] = a.S0 ? a.S0[(static_cast<size_t>(bh) * D + 16 * w + 4 * q + e) * D + c0 + r] : 0.f;
+  *reinterpret_cast<float4 *>(&sSt[0][r * LT + 16 * w + 4 * q]) = make_float4(S[0], S[1], S[2], S[3]);
+  FwdA A;
+  FwdB Bf;
+  loadA(A, 0);
+  loadB(Bf, 0);
   __syncthreads();
-  auto step = [&](FwdA &A, FwdB &Bf, int c) __attribute__((always_inline)) {
-    const int p = c & 1, cn = min(c + 2, a.NC - 1);   // the last steps reload a chunk of their own
+  for (int c = 0; c < a.NC; ++c) {
+    const int p = c & 1, cn = min(c + 1, a.NC - 1);   // the last step reloads its own chunk
     float *rec = recs + static_cast<size_t>(c) * REC;
-    float *sin = a.sin + (static_cast<size_t>(bh) * a.NC + c) * D * D;
-#pragma unroll
-    for (int x = 0; x < 2; ++x) {   // the entering state, rows of 16 columns from its LDS copy
-      const int idx = tid + 256 * x, i = idx >> 2, c4 = (idx & 3) * 4;
+    {   // the entering state, rows of 16 columns from its LDS copy
+      float *sin = a.sin + (static_cast<size_t>(bh) * a.NC + c) * D * D;
+      const int i = tid >> 2, c4 = (tid & 3) * 4;
       const float *src = &sSt[p][c4 * LT + i];
-      *reinterpret_cast<float4 *>(sin + i * D + c0 + c4) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
+      *reinterpret_cast<float4 *>(sin + cblk(i, c0 + c4, D)) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
     }
-    // U = U~ - W S, rows 16w.. (two accumulation chains)
-    const float *bs = &sSt[p][r * LT + 4 * q];
+    // partial U over this wave's half of the contraction
+    const float *bs = &sSt[p][r * LT + 64 * kh + 4 * q];
     f32x4 u0 = zero4(), u1 = zero4();
-#pragma unroll
-    for (int kb = 0; kb < 8; kb += 2) {
-      u0 = mma16(u0, A.w[kb], ld4(bs + 16 * kb));
-      u1 = mma16(u1, A.w[kb + 1], ld4(bs + 16 * kb + 16));
-    }
+    u0 = mma16(u0, A.w[0], ld4(bs));
+    u1 = mma16(u1, A.w[1], ld4(bs + 16));
+    u0 = mma16(u0, A.w[2], ld4(bs + 32));
+    u1 = mma16(u1, A.w[3], ld4(bs + 48));
     float u[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) u[e] = A.ut[e] - (u0[e] + u1[e]);
-    *reinterpret_cast<float4 *>(&sUt[p][r * LU + 16 * w + 4 * q]) = make_float4(u[0], u[1], u[2], u[3]);
+    for (int e = 0; e < 4; ++e) u[e] = (kh == 0 ? A.ut[e] : 0.f) - (u0[e] + u1[e]);
+    *reinterpret_cast<float4 *>(&sUt[p][kh][r * LU + 16 * ta + 4 * q]) = make_float4(u[0], u[1], u[2], u[3]);
     loadA(A, cn);
     lds_barrier();
-    {   // U replaces U~ (its columns are this workgroup's alone), rows from the LDS copy
+    if (tid < 256) {   // U replaces U~ (its columns are this workgroup's alone)
       const int t = tid >> 2, c4 = (tid & 3) * 4;
-      const float *src = &sUt[p][c4 * LU + t];
-      *reinterpret_cast<float4 *>(rec + R_UT + t * D + c0 + c4) = make_float4(src[0], src[LU], src[2 * LU], src[3 * LU]);
+      const float *s0p = &sUt[p][0][c4 * LU + t], *s1p = &sUt[p][1][c4 * LU + t];
+      *reinterpret_cast<float4 *>(rec + R_UT + cblk(t, c0 + c4, C)) =
+          make_float4(s0p[0] + s1p[0], s0p[LU] + s1p[LU], s0p[2 * LU] + s1p[2 * LU], s0p[3 * LU] + s1p[3 * LU]);
     }
-    // S = D S + K_dec^T U
-    const float *bu = &sUt[p][r * LU + 4 * q];
+    // S = D S + K_dec^T U, rows 16w..
+    const float *bu0 = &sUt[p][0][r * LU + 4 * q], *bu1 = &sUt[p][1][r * LU + 4 * q];
+    f32x4 s0, s1 = zero4();
+    s0[0] = Bf.d.x * S[0];
+    s0[1] = Bf.d.y * S[1];
+    s0[2] = Bf.d.z * S[2];
+    s0[3] = Bf.d.w * S[3];
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      f32x4 s0, s1 = zero4();
-      s0[0] = Bf.d[it].x * S[it][0];
-      s0[1] = Bf.d[it].y * S[it][1];
-      s0[2] = Bf.d[it].z * S[it][2];
-      s0[3] = Bf.d[it].w * S[it][3];
-#pragma unroll
-      for (int kb = 0; kb < 4; kb += 2) {
-        s0 = mma16(s0, Bf.kd[it][kb], ld4(bu + 16 * kb));
-        s1 = mma16(s1, Bf.kd[it][kb + 1], ld4(bu + 16 * kb + 16));
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) S[it][e] = s0[e] + s1[e];
-      *reinterpret_cast<float4 *>(&sSt[p ^ 1][r * LT + 16 * (w + 4 * it) + 4 * q]) =
-          make_float4(S[it][0], S[it][1], S[it][2], S[it][3]);
+    for (int kb = 0; kb < 4; kb += 2) {
+      const float4 x0 = ld4(bu0 + 16 * kb), y0 = ld4(bu1 + 16 * kb);
+      const float4 x1 = ld4(bu0 + 16 * kb + 16), y1 = ld4(bu1 + 16 * kb + 16);
+      s0 = mma16(s0, Bf.kd[kb], make_float4(x0.x + y0.x, x0.y + y0.y, x0.z + y0.z, x0.w + y0.w));
+      s1 = mma16(s1, Bf.kd[kb + 1], make_float4(x1.x + y1.x, x1.y + y1.y, x1.z + y1.z, x1.w + y1.w));
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[e] = s0[e] + s1[e];
+    *reinterpret_cast<float4 *>(&sSt[p ^ 1][r * LT + 16 * w + 4 * q]) = make_float4(S[0], S[1], S[2], S[3]);
     loadB(Bf, cn);
     lds_barrier();
-  };
-  // both steps unconditional in the loop (an odd last chunk runs after it), so that the
-  // compiler's wait counts for the prefetched sets stay exact across the back edge
-  int c = 0;
-  for (; c + 1 < a.NC; c += 2) {
-    step(A0, B0, c);
-    step(A1, B1, c + 1);
   }
-  if (c < a.NC) step(A0, B0, c);
 }
 
 // ---------------------------------------------------------------------------
 // bwd_rev: dS after every chunk (reverse order), dU, and dS0
 // ---------------------------------------------------------------------------
-// Phases dU = P^T dO + K_dec dS (rows 16w..) and dS = D dS + Q~^T dO - W^T dU, with the
-// record fragments of the next (earlier) chunk loaded one phase ahead and its dO block
-// one step ahead.  dS, dO and dU blocks are kept in LDS transposed and double buffered.
-// (D rides with the phase-A fragments: loaded half a step earlier than the phase-B set,
-// its early use does not wait for that set)
-struct RevA { float4 p[4]; float4 kd[8]; float4 d[2]; };
-struct RevB { float4 qt[2][4]; float4 wt[2][4]; };
+// Eight waves per unit, as the state sweep.  Phases: dU = P^T dO + K_dec dS (wave w: rows
+// 16(w&3).. of dU; the twelve 16-long blocks of the contraction split six and six by
+// (w>>2)), then dS = D dS + Q~^T dO - W^T dU (wave w: rows 16w..).  Record fragments and
+// the dO block of the next (earlier) chunk are loaded one step ahead (D with the phase-A
+// set, so that its early use does not wait for the phase-B set); dS, dO and the two
+// partial sums of dU are kept in LDS transposed and double buffered.
+struct RevA { float4 f[6]; float4 d; };
+struct RevB { float4 qt[4]; float4 wt[4]; };
 
-__global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void bwd_rev(BwdArgs a) {
   __shared__ __align__(16) float sdSt[2][16 * LT];
   __shared__ __align__(16) float sdOt[2][16 * LU];
-  __shared__ __align__(16) float sdUt[2][16 * LU];
+  __shared__ __align__(16) float sdUt[2][2][16 * LU];
   int bh, cb;
   if (!sweep_unit(a.B * a.H, bh, cb)) return;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, q = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ta = w & 3, kh = w >> 2;
   const int c0 = 16 * cb, b = bh / a.H, h = bh % a.H;
   const float *recs = a.rec + static_cast<size_t>(bh) * a.NC * REC;
+  // contraction blocks of dU: kh = 0 takes P^T blocks 0..3 (over t) and K_dec blocks 0..1
+  // (over i); kh = 1 takes K_dec blocks 2..7
   auto loadA = [&](RevA &x, int c) {
     const float *rec = recs + static_cast<size_t>(c) * REC;
+    if (kh == 0) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)   // P^T[t'][t] (zero for t < t')
-      x.p[kb] = ld4(rec + R_PT + (16 * w + r) * C + 16 * kb + 4 * q);
+      for (int j = 0; j < 4; ++j) x.f[j] = ld4(rec + R_PT + (16 * ta + r) * C + 16 * j + 4 * q);
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) x.kd[kb] = ld4(rec + R_KD + (16 * w + r) * D + 16 * kb + 4 * q);
+      for (int j = 0; j < 2; ++j) x.f[4 + j] = ld4(rec + R_KD + (16 * ta + r) * D + 16 * j + 4 * q);
+    } else {
 #pragma unroll
-    for (int it = 0; it < 2; ++it) x.d[it] = ld4(rec + R_D + 16 * (w + 4 * it) + 4 * q);
+      for (int j = 0; j < 6; ++j) x.f[j] = ld4(rec + R_KD + (16 * ta + r) * D + 16 * (j + 2) + 4 * q);
+    }
+    x.d = ld4(rec + R_D + 16 * w + 4 * q);
   };
   auto loadB = [&](RevB &x, int c) {
     const float *rec = recs + static_cast<size_t>(c) * REC;
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int ib = 16 * (w + 4 * it);
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        x.qt[it][kb] = col4(rec + R_QT + (16 * kb + 4 * q) * D + ib + r, D);
-        x.wt[it][kb] = ld4(rec + R_WT + (ib + r) * C + 16 * kb + 4 * q);
-      }
+    for (int kb = 0; kb < 4; ++kb) {
+      x.qt[kb] = col4(rec + R_QT + (16 * kb + 4 * q) * D + 16 * w + r, D);
+      x.wt[kb] = ld4(rec + R_WT + (16 * w + r) * C + 16 * kb + 4 * q);
     }
   };
-  // one float4 of a chunk's dO block [64][16] per thread (rows past the end read 0),
-  // stored transposed
-  const int ot = tid >> 2, ox = (tid & 3) * 4;
+  // one float4 of a chunk's dO block [64][16] for each of the first 256 threads (rows
+  // past the end read 0), stored transposed
+  const int ot = (tid & 255) >> 2, ox = (tid & 3) * 4;
   auto loadO = [&](int c) {
     const int t = c * C + ot;
     float4 v = ld4(a.dO + tok_off(a, b, h, min(t, a.T - 1)) + c0 + ox);
@@ -510,22 +499,18 @@ __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
     return v;
   };
   auto storeO = [&](float *dst, float4 v) {
-    dst[(ox + 0) * LU + ot] = v.x;
-    dst[(ox + 1) * LU + ot] = v.y;
-    dst[(ox + 2) * LU + ot] = v.z;
-    dst[(ox + 3) * LU + ot] = v.w;
-  };
-  f32x4 dS[2];
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * (w + 4 * it) + 4 * q + e;
-      dS[it][e] = a.dSf ? a.dSf[(static_cast<size_t>(bh) * D + i) * D + c0 + r] : 0.f;
+    if (tid < 256) {
+      dst[(ox + 0) * LU + ot] = v.x;
+      dst[(ox + 1) * LU + ot] = v.y;
+      dst[(ox + 2) * LU + ot] = v.z;
+      dst[(ox + 3) * LU + ot] = v.w;
     }
-    *reinterpret_cast<float4 *>(&sdSt[0][r * LT + 16 * (w + 4 * it) + 4 * q]) =
-        make_float4(dS[it][0], dS[it][1], dS[it][2], dS[it][3]);
-  }
+  };
+  f32x4 dS;
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    dS[e] = a.dSf ? a.dSf[(static_cast<size_t>(bh) * D + 16 * w + 4 * q + e) * D + c0 + r] : 0.f;
+  *reinterpret_cast<float4 *>(&sdSt[0][r * LT + 16 * w + 4 * q]) = make_float4(dS[0], dS[1], dS[2], dS[3]);
   if (a.NC > 0) {
     RevA A;
     RevB Bf;
@@ -535,59 +520,60 @@ __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
     __syncthreads();
     for (int c = a.NC - 1, p = 0; c >= 0; --c, p ^= 1) {
       const int cn = max(c - 1, 0);   // the last step reloads its own chunk
-      float *dsa = a.dsa + (static_cast<size_t>(bh) * a.NC + c) * D * D;
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {   // dS after this chunk, rows of 16 columns from its LDS copy
-        const int idx = tid + 256 * x, i = idx >> 2, c4 = (idx & 3) * 4;
+      {   // dS after this chunk, rows of 16 columns from its LDS copy
+        float *dsa = a.dsa + (static_cast<size_t>(bh) * a.NC + c) * D * D;
+        const int i = tid >> 2, c4 = (tid & 3) * 4;
         const float *src = &sdSt[p][c4 * LT + i];
-        *reinterpret_cast<float4 *>(dsa + i * D + c0 + c4) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
+        *reinterpret_cast<float4 *>(dsa + cblk(i, c0 + c4, D)) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
       }
       const float4 ov = loadO(cn);
-      // dU = P^T dO + K_dec dS, rows 16w.. (two accumulation chains)
-      const float *bo = &sdOt[p][r * LU + 4 * q], *bs = &sdSt[p][r * LT + 4 * q];
+      // partial dU over this wave's six contraction blocks
       f32x4 u0 = zero4(), u1 = zero4();
+      if (kh == 0) {
+        const float *bo = &sdOt[p][r * LU + 4 * q], *bs = &sdSt[p][r * LT + 4 * q];
+        u0 = mma16(u0, A.f[0], ld4(bo));
+        u1 = mma16(u1, A.f[1], ld4(bo + 16));
+        u0 = mma16(u0, A.f[2], ld4(bo + 32));
+        u1 = mma16(u1, A.f[3], ld4(bo + 48));
+        u0 = mma16(u0, A.f[4], ld4(bs));
+        u1 = mma16(u1, A.f[5], ld4(bs + 16));
+      } else {
+        const float *bs = &sdSt[p][r * LT + 32 + 4 * q];
 #pragma unroll
-      for (int kb = 0; kb < 4; kb += 2) {
-        u0 = mma16(u0, A.p[kb], ld4(bo + 16 * kb));
-        u1 = mma16(u1, A.p[kb + 1], ld4(bo + 16 * kb + 16));
+        for (int j = 0; j < 6; j += 2) {
+          u0 = mma16(u0, A.f[j], ld4(bs + 16 * j));
+          u1 = mma16(u1, A.f[j + 1], ld4(bs + 16 * j + 16));
+        }
       }
-#pragma unroll
-      for (int kb = 0; kb < 8; kb += 2) {
-        u0 = mma16(u0, A.kd[kb], ld4(bs + 16 * kb));
-        u1 = mma16(u1, A.kd[kb + 1], ld4(bs + 16 * kb + 16));
-      }
-      float uu[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) uu[e] = u0[e] + u1[e];
-      *reinterpret_cast<float4 *>(&sdUt[p][r * LU + 16 * w + 4 * q]) = make_float4(uu[0], uu[1], uu[2], uu[3]);
-      const float4 dcur[2] = {A.d[0], A.d[1]};
+      *reinterpret_cast<float4 *>(&sdUt[p][kh][r * LU + 16 * ta + 4 * q]) =
+          make_float4(u0[0] + u1[0], u0[1] + u1[1], u0[2] + u1[2], u0[3] + u1[3]);
+      const float4 dcur = A.d;
       loadA(A, cn);
       lds_barrier();
-      {   // dU rows from the LDS copy
+      if (tid < 256) {   // dU rows from the LDS partial sums
         float *du = a.du + (static_cast<size_t>(bh) * a.NC + c) * C * D;
         const int t = tid >> 2, c4 = (tid & 3) * 4;
-        const float *src = &sdUt[p][c4 * LU + t];
-        *reinterpret_cast<float4 *>(du + t * D + c0 + c4) = make_float4(src[0], src[LU], src[2 * LU], src[3 * LU]);
+        const float *s0p = &sdUt[p][0][c4 * LU + t], *s1p = &sdUt[p][1][c4 * LU + t];
+        *reinterpret_cast<float4 *>(du + cblk(t, c0 + c4, C)) =
+            make_float4(s0p[0] + s1p[0], s0p[LU] + s1p[LU], s0p[2 * LU] + s1p[2 * LU], s0p[3 * LU] + s1p[3 * LU]);
       }
-      // dS = D dS + Q~^T dO - W^T dU
-      const float *bu = &sdUt[p][r * LU + 4 * q];
+      // dS = D dS + Q~^T dO - W^T dU, rows 16w..
+      const float *bo = &sdOt[p][r * LU + 4 * q];
+      const float *bu0 = &sdUt[p][0][r * LU + 4 * q], *bu1 = &sdUt[p][1][r * LU + 4 * q];
+      f32x4 s0, s1 = zero4();
+      s0[0] = dcur.x * dS[0];
+      s0[1] = dcur.y * dS[1];
+      s0[2] = dcur.z * dS[2];
+      s0[3] = dcur.w * dS[3];
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        f32x4 s0, s1 = zero4();
-        s0[0] = dcur[it].x * dS[it][0];
-        s0[1] = dcur[it].y * dS[it][1];
-        s0[2] = dcur[it].z * dS[it][2];
-        s0[3] = dcur[it].w * dS[it][3];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          s0 = mma16(s0, Bf.qt[it][kb], ld4(bo + 16 * kb));
-          s1 = mma16(s1, Bf.wt[it][kb], neg4(ld4(bu + 16 * kb)));
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dS[it][e] = s0[e] + s1[e];
-        *reinterpret_cast<float4 *>(&sdSt[p ^ 1][r * LT + 16 * (w + 4 * it) + 4 * q]) =
-            make_float4(dS[it][0], dS[it][1], dS[it][2], dS[it][3]);
+      for (int kb = 0; kb < 4; ++kb) {
+        const float4 x = ld4(bu0 + 16 * kb), y = ld4(bu1 + 16 * kb);
+        s0 = mma16(s0, Bf.qt[kb], ld4(bo + 16 * kb));
+        s1 = mma16(s1, Bf.wt[kb], make_float4(-(x.x + y.x), -(x.y + y.y), -(x.z + y.z), -(x.w + y.w)));
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dS[e] = s0[e] + s1[e];
+      *reinterpret_cast<float4 *>(&sdSt[p ^ 1][r * LT + 16 * w + 4 * q]) = make_float4(dS[0], dS[1], dS[2], dS[3]);
       storeO(sdOt[p ^ 1], ov);
       loadB(Bf, cn);
       lds_barrier();
@@ -595,10 +581,8 @@ __global__ __launch_bounds__(256) void bwd_rev(BwdArgs a) {
   }
   if (a.dS0)
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        a.dS0[(static_cast<size_t>(bh) * D + 16 * (w + 4 * it) + 4 * q + e) * D + c0 + r] = dS[it][e];
+    for (int e = 0; e < 4; ++e)
+      a.dS0[(static_cast<size_t>(bh) * D + 16 * w + 4 * q + e) * D + c0 + r] = dS[e];
 }
 
 // ---------------------------------------------------------------------------
@@ -642,8 +626,8 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
     const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
     vo[x] = ld4(a.dO + tok_off(a, b, h, t0 + min(t, Tc - 1)) + i);
     if (t >= Tc) vo[x] = make_float4(0.f, 0.f, 0.f, 0.f);
-    vu[x] = ld4(Ug + t * D + i);
-    vd[x] = ld4(dUg + t * D + i);
+    vu[x] = ld4(Ug + 4 * e);    // column-blocked: consecutive threads, consecutive bytes
+    vd[x] = ld4(dUg + 4 * e);
   }
 #pragma unroll
   for (int x = 0; x < 2; ++x) vm[x] = ld4(rec + R_M + 4 * (tid + 512 * x));
@@ -667,8 +651,9 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
   for (int x = 0; x < 4; ++x) {
     const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
     *reinterpret_cast<float4 *>(s3 + t * LD + i) = vo[x];
-    *reinterpret_cast<float4 *>(s1 + t * LD + i) = vu[x];
-    *reinterpret_cast<float4 *>(s2 + t * LD + i) = vd[x];
+    const int tb = (e >> 2) & (C - 1), ib = 16 * (e >> 8) + 4 * (e & 3);   // element 4e, blocked
+    *reinterpret_cast<float4 *>(s1 + tb * LD + ib) = vu[x];
+    *reinterpret_cast<float4 *>(s2 + tb * LD + ib) = vd[x];
   }
 #pragma unroll
   for (int x = 0; x < 2; ++x) {
@@ -712,7 +697,7 @@ __global__ __launch_bounds__(512, 1) void bwd_grad(BwdArgs a) {
   {
     auto load_bt = [&](float4 (&bt4)[4], const float *X, int kb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bt4[i] = ld4(X + col(i) * D + 16 * kb + 4 * q);
+      for (int i = 0; i < 4; ++i) bt4[i] = ld4(X + kb * D * 16 + col(i) * 16 + 4 * q);   // (col(i), 16 kb + 4q)
     };
     float4 sc[4], sn[4], dc[4], dn[4];
     load_bt(sc, S, 0);
@@ -1050,11 +1035,11 @@ hipError_t launch_backward(const kda_backward_desc &d, hipStream_t s) {
   }
   const unsigned sweep_grid = static_cast<unsigned>((BH + 7) / 8 * 64);
   if (nch > 0) {
-    bwd_fwd<<<dim3(sweep_grid), dim3(256), 0, s>>>(a);
+    bwd_fwd<<<dim3(sweep_grid), dim3(512), 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  bwd_rev<<<dim3(sweep_grid), dim3(256), 0, s>>>(a);
+  bwd_rev<<<dim3(sweep_grid), dim3(512), 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nch > 0) {
