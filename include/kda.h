@@ -236,7 +236,7 @@ typedef struct kda_backward_desc {
   float *dbeta;             /* [B,T,H] */
   float *dS0;               /* [B,H,d_k,d_v], or NULL when not wanted */
   void *workspace;          /* device scratch of kda_backward_workspace_size() bytes:
-                               400.5 KiB per 64-token chunk and head (chunk
+                               368.5 KiB per 64-token chunk and head (chunk
                                quantities, the state and its gradient at every chunk
                                boundary, and the chunk's dL/dU) */
   size_t workspace_bytes;

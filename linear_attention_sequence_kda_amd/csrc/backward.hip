@@ -39,13 +39,13 @@ constexpr int LD = D + 4;     // LDS row stride of [C][D] tiles
 constexpr int LS = C + 4;     // LDS row stride of [C][C] tiles
 constexpr int LV = 20;        // LDS row stride of [*][16] column blocks
 
-// per-chunk record, floats.  P and W are also kept transposed, where that costs the
-// chunk kernel nothing (its MFMA output fragments hold four consecutive rows).
+// per-chunk record, floats.  P is kept transposed (the chunk kernel's MFMA output
+// fragments hold four consecutive rows of it, the gradient sweep reads its columns).
 constexpr int R_G = 0;                // [C][D] G in log2 units
 constexpr int R_KD = R_G + C * D;     // [C][D] K_dec
 constexpr int R_W = R_KD + C * D;     // [C][D] W
-constexpr int R_WT = R_W + C * D;     // [D][C] W^T
-constexpr int R_UT = R_WT + C * D;    // [C][D] U~, replaced by U = U~ - W S in the state sweep
+constexpr int R_UT = R_W + C * D;     // [C][D] U~ (column-blocked), replaced by U = U~ - W S
+                                      // in the state sweep
 constexpr int R_QT = R_UT + C * D;    // [C][D] Q~
 constexpr int R_PT = R_QT + C * D;    // [C][C] P^T (zero below the diagonal)
 constexpr int R_M = R_PT + C * C;     // [C][C] M (zero above the diagonal)
@@ -328,8 +328,6 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
       rec[R_W + t * D + n] = accW[i][e];
       rec[R_UT + cblk(t, n, C)] = accU[i][e];
     }
-    *reinterpret_cast<float4 *>(rec + R_WT + n * C + 16 * tm + 4 * q) =
-        make_float4(accW[i][0], accW[i][1], accW[i][2], accW[i][3]);
   }
 }
 
@@ -396,12 +394,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void b
   for (int c = 0; c < a.NC; ++c) {
     const int p = c & 1, cn = min(c + 1, a.NC - 1);   // the last step reloads its own chunk
     float *rec = recs + static_cast<size_t>(c) * REC;
-    {   // the entering state, rows of 16 columns from its LDS copy
-      float *sin = a.sin + (static_cast<size_t>(bh) * a.NC + c) * D * D;
-      const int i = tid >> 2, c4 = (tid & 3) * 4;
-      const float *src = &sSt[p][c4 * LT + i];
-      *reinterpret_cast<float4 *>(sin + cblk(i, c0 + c4, D)) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
-    }
     // partial U over this wave's half of the contraction
     const float *bs = &sSt[p][r * LT + 64 * kh + 4 * q];
     f32x4 u0 = zero4(), u1 = zero4();
@@ -439,6 +431,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void b
     for (int e = 0; e < 4; ++e) S[e] = s0[e] + s1[e];
     *reinterpret_cast<float4 *>(&sSt[p ^ 1][r * LT + 16 * w + 4 * q]) = make_float4(S[0], S[1], S[2], S[3]);
     loadB(Bf, cn);
+    {   // the state entering this chunk, rows of 16 columns from its LDS copy (unchanged
+        // this step).  Issued after the prefetches: the wait counter completes in issue
+        // order, so no wait for a prefetched fragment also waits for this store.
+      float *sin = a.sin + (static_cast<size_t>(bh) * a.NC + c) * D * D;
+      const int i = tid >> 2, c4 = (tid & 3) * 4;
+      const float *src = &sSt[p][c4 * LT + i];
+      *reinterpret_cast<float4 *>(sin + cblk(i, c0 + c4, D)) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
+    }
     lds_barrier();
   }
 }
@@ -486,7 +486,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void b
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       x.qt[kb] = col4(rec + R_QT + (16 * kb + 4 * q) * D + 16 * w + r, D);
-      x.wt[kb] = ld4(rec + R_WT + (16 * w + r) * C + 16 * kb + 4 * q);
+      x.wt[kb] = col4(rec + R_W + (16 * kb + 4 * q) * D + 16 * w + r, D);
     }
   };
   // one float4 of a chunk's dO block [64][16] for each of the first 256 threads (rows
@@ -520,12 +520,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void b
     __syncthreads();
     for (int c = a.NC - 1, p = 0; c >= 0; --c, p ^= 1) {
       const int cn = max(c - 1, 0);   // the last step reloads its own chunk
-      {   // dS after this chunk, rows of 16 columns from its LDS copy
-        float *dsa = a.dsa + (static_cast<size_t>(bh) * a.NC + c) * D * D;
-        const int i = tid >> 2, c4 = (tid & 3) * 4;
-        const float *src = &sdSt[p][c4 * LT + i];
-        *reinterpret_cast<float4 *>(dsa + cblk(i, c0 + c4, D)) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
-      }
       const float4 ov = loadO(cn);
       // partial dU over this wave's six contraction blocks
       f32x4 u0 = zero4(), u1 = zero4();
@@ -576,6 +570,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void b
       *reinterpret_cast<float4 *>(&sdSt[p ^ 1][r * LT + 16 * w + 4 * q]) = make_float4(dS[0], dS[1], dS[2], dS[3]);
       storeO(sdOt[p ^ 1], ov);
       loadB(Bf, cn);
+      {   // dS after this chunk (unchanged this step), after the prefetches as in the
+          // state sweep
+        float *dsa = a.dsa + (static_cast<size_t>(bh) * a.NC + c) * D * D;
+        const int i = tid >> 2, c4 = (tid & 3) * 4;
+        const float *src = &sdSt[p][c4 * LT + i];
+        *reinterpret_cast<float4 *>(dsa + cblk(i, c0 + c4, D)) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
+      }
       lds_barrier();
     }
   }

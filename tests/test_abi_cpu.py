@@ -202,7 +202,7 @@ def test_backward_workspace_size():
     n = C.c_size_t(0)
     assert lib.kda_backward_workspace_size(C.byref(_bdesc()), C.byref(n)) == kda.KDA_OK
     # 2 chunks per sequence (T = 100), 2 x 3 heads: record + state + state gradient + dU
-    rec = 6 * 64 * 128 + 3 * 64 * 64 + 128
+    rec = 5 * 64 * 128 + 3 * 64 * 64 + 128
     assert n.value == 2 * 3 * 2 * (rec + 2 * 128 * 128 + 64 * 128) * 4
     assert lib.kda_backward_workspace_size(C.byref(_bdesc(T=0)), C.byref(n)) == kda.KDA_OK
     assert n.value == 0
