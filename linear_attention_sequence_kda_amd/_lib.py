@@ -318,6 +318,17 @@ def kda_prefill_backward(q, k, v, g, beta, dO, *, dq, dk, dv, dg, dbeta, S0=None
     dS_final, dS0: [B,H,128,128] float32 or None.  dq, dk, dv, dg: [B,T,H,128] float32;
     dbeta: [B,T,H] float32.  Without a workspace, one is allocated from torch's caching
     allocator."""
+    B, T, H, dk_ = q.shape
+    for name, t, shape in (("dO", dO, (B, T, H, v.shape[-1])), ("dq", dq, q.shape), ("dk", dk, q.shape),
+                           ("dv", dv, v.shape), ("dg", dg, g.shape), ("dbeta", dbeta, beta.shape),
+                           ("S0", S0, (B, H, dk_, v.shape[-1])), ("dS_final", dS_final, (B, H, dk_, v.shape[-1])),
+                           ("dS0", dS0, (B, H, dk_, v.shape[-1]))):
+        if t is None:
+            continue
+        if t.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if workspace is None:
         n = kda_backward_workspace_size(q, k, v, g, beta, dO, chunk=chunk)
         if n > 0:

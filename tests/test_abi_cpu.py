@@ -232,3 +232,20 @@ def test_backward_validation_errors():
     d.workspace = d.dv                           # workspace over an output
     assert f(d) == kda.KDA_ERR_ALIAS
     assert f(_bdesc(B=0)) == kda.KDA_OK          # nothing to do
+
+
+def test_backward_binding_checks_dtypes_and_shapes():
+    """The binding rejects a wrong dtype or shape before any pointer reaches the library
+    (tensors on the CPU never get that far either: the device check comes later)."""
+    import torch
+    B, T, H = 1, 5, 1
+    q = torch.zeros(B, T, H, 128)
+    g = torch.zeros(B, T, H, 128)
+    beta = torch.zeros(B, T, H)
+    good = dict(dq=torch.zeros(B, T, H, 128), dk=torch.zeros(B, T, H, 128),
+                dv=torch.zeros(B, T, H, 128), dg=torch.zeros(B, T, H, 128), dbeta=torch.zeros(B, T, H))
+    with pytest.raises(ValueError, match="dO must be float32"):
+        kda.kda_prefill_backward(q, q, q, g, beta, torch.zeros(B, T, H, 128, dtype=torch.bfloat16), **good)
+    bad = dict(good, dbeta=torch.zeros(B, T, H, 1))
+    with pytest.raises(ValueError, match="dbeta has shape"):
+        kda.kda_prefill_backward(q, q, q, g, beta, torch.zeros(B, T, H, 128), **bad)
