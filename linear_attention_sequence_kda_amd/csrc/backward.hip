@@ -331,48 +331,55 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
   }
 }
 
-// (sequence, head) and 16-column block of a sweep workgroup.  The eight column blocks of
-// a (sequence, head) share one XCD (workgroups are dealt to XCDs round robin), so the
-// chunk records they all read are fetched into one L2.
+// (sequence, head) and column unit of a sweep workgroup (NU units of 128/NU columns per
+// head).  The units of a (sequence, head) share one XCD (workgroups are dealt to XCDs
+// round robin), so the chunk records they all read are fetched into one L2.
+template <int NU>
 __device__ __forceinline__ bool sweep_unit(int BH, int &bh, int &cb) {
   const int x = blockIdx.x, xcd = x & 7, slot = x >> 3;
-  bh = (slot >> 3) * 8 + xcd;
-  cb = slot & 7;
+  bh = (slot / NU) * 8 + xcd;
+  cb = slot % NU;
   return bh < BH;
 }
 
 // ---------------------------------------------------------------------------
-// bwd_fwd: states entering every chunk, for 16 value columns of one (sequence, head)
+// bwd_fwd: states entering every chunk, for 16 CB value columns of one (sequence, head)
 // ---------------------------------------------------------------------------
 // Eight waves per unit.  Each chunk step has two phases: U = U~ - W S (wave w: rows
-// 16(w&3).. of U over half of the contraction, (w>>2)), then S = D S + K_dec^T U (wave w:
-// state rows 16w..).  The record fragments of a phase are loaded one step ahead, so their
-// latency overlaps the other phase; with 128 registers two units share a CU (16 waves).
-// S and the two partial sums of U are kept in LDS transposed ([column][row],
-// double buffered), so that an MFMA operand is one 16-byte read and a step needs two
-// barriers; state and U rows go to global memory as 16-byte stores from those copies.
+// 16(w&3).. of U over half of the contraction, (w>>2), for all CB column blocks), then
+// S = D S + K_dec^T U (wave w: state rows 16w..).  The record fragments of a phase are
+// loaded one step ahead, so their latency overlaps the other phase, and each fragment
+// serves the unit's CB column blocks (the record is read once per 16 CB columns).  S and
+// the two partial sums of U are kept in LDS transposed ([column][row], double buffered),
+// so that an MFMA operand is one 16-byte read and a step needs two barriers; state and U
+// rows go to global memory as 16-byte stores from those copies.
 constexpr int LT = D + 4;   // row stride of a transposed [16][D] block
 constexpr int LU = C + 4;   // row stride of a transposed [16][C] block
+constexpr int SWEEP_CB = 2; // 16-column blocks per sweep unit
 
-struct FwdA { float4 w[4]; float ut[4]; };
+template <int CB> struct FwdA { float4 w[4]; float ut[CB][4]; };
 struct FwdB { float4 kd[4]; float4 d; };
 
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void bwd_fwd(BwdArgs a) {
-  __shared__ __align__(16) float sSt[2][16 * LT];
-  __shared__ __align__(16) float sUt[2][2][16 * LU];
+template <int CB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4 / CB))) void bwd_fwd(BwdArgs a) {
+  constexpr int NU = 8 / CB, NCOL = 16 * CB;
+  __shared__ __align__(16) float sSt[2][NCOL * LT];
+  __shared__ __align__(16) float sUt[2][2][NCOL * LU];
   int bh, cb;
-  if (!sweep_unit(a.B * a.H, bh, cb)) return;
+  if (!sweep_unit<NU>(a.B * a.H, bh, cb)) return;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, q = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ta = w & 3, kh = w >> 2;
-  const int c0 = 16 * cb;
+  const int c0 = NCOL * cb;
   float *recs = a.rec + static_cast<size_t>(bh) * a.NC * REC;
-  auto loadA = [&](FwdA &x, int c) {
+  auto loadA = [&](FwdA<CB> &x, int c) {
     const float *rec = recs + static_cast<size_t>(c) * REC;
 #pragma unroll
     for (int j = 0; j < 4; ++j) x.w[j] = ld4(rec + R_W + (16 * ta + r) * D + 16 * (4 * kh + j) + 4 * q);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x.ut[e] = rec[R_UT + cblk(16 * ta + 4 * q + e, c0 + r, C)];
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x.ut[j][e] = rec[R_UT + cblk(16 * ta + 4 * q + e, c0 + 16 * j + r, C)];
   };
   auto loadB = [&](FwdB &x, int c) {
     const float *rec = recs + static_cast<size_t>(c) * REC;
@@ -380,13 +387,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void b
     for (int kb = 0; kb < 4; ++kb) x.kd[kb] = col4(rec + R_KD + (16 * kb + 4 * q) * D + 16 * w + r, D);
     x.d = ld4(rec + R_D + 16 * w + 4 * q);
   };
-  // state rows 16w + 4q + e, column c0 + r
-  f32x4 S;
+  // state rows 16w + 4q + e, columns c0 + 16j + r
+  f32x4 S[CB];
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    S[e] = a.S0 ? a.S0[(static_cast<size_t>(bh) * D + 16 * w + 4 * q + e) * D + c0 + r] : 0.f;
-  *reinterpret_cast<float4 *>(&sSt[0][r * LT + 16 * w + 4 * q]) = make_float4(S[0], S[1], S[2], S[3]);
-  FwdA A;
+  for (int j = 0; j < CB; ++j) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      S[j][e] = a.S0 ? a.S0[(static_cast<size_t>(bh) * D + 16 * w + 4 * q + e) * D + c0 + 16 * j + r] : 0.f;
+    *reinterpret_cast<float4 *>(&sSt[0][(16 * j + r) * LT + 16 * w + 4 * q]) = make_float4(S[j][0], S[j][1], S[j][2], S[j][3]);
+  }
+  FwdA<CB> A;
   FwdB Bf;
   loadA(A, 0);
   loadB(Bf, 0);
@@ -394,50 +404,60 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void b
   for (int c = 0; c < a.NC; ++c) {
     const int p = c & 1, cn = min(c + 1, a.NC - 1);   // the last step reloads its own chunk
     float *rec = recs + static_cast<size_t>(c) * REC;
-    // partial U over this wave's half of the contraction
-    const float *bs = &sSt[p][r * LT + 64 * kh + 4 * q];
-    f32x4 u0 = zero4(), u1 = zero4();
-    u0 = mma16(u0, A.w[0], ld4(bs));
-    u1 = mma16(u1, A.w[1], ld4(bs + 16));
-    u0 = mma16(u0, A.w[2], ld4(bs + 32));
-    u1 = mma16(u1, A.w[3], ld4(bs + 48));
-    float u[4];
+    // partial U over this wave's half of the contraction (two chains per column block)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) u[e] = (kh == 0 ? A.ut[e] : 0.f) - (u0[e] + u1[e]);
-    *reinterpret_cast<float4 *>(&sUt[p][kh][r * LU + 16 * ta + 4 * q]) = make_float4(u[0], u[1], u[2], u[3]);
+    for (int j = 0; j < CB; ++j) {
+      const float *bs = &sSt[p][(16 * j + r) * LT + 64 * kh + 4 * q];
+      f32x4 u0 = zero4(), u1 = zero4();
+      u0 = mma16(u0, A.w[0], ld4(bs));
+      u1 = mma16(u1, A.w[1], ld4(bs + 16));
+      u0 = mma16(u0, A.w[2], ld4(bs + 32));
+      u1 = mma16(u1, A.w[3], ld4(bs + 48));
+      float u[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = (kh == 0 ? A.ut[j][e] : 0.f) - (u0[e] + u1[e]);
+      *reinterpret_cast<float4 *>(&sUt[p][kh][(16 * j + r) * LU + 16 * ta + 4 * q]) = make_float4(u[0], u[1], u[2], u[3]);
+    }
     loadA(A, cn);
     lds_barrier();
-    if (tid < 256) {   // U replaces U~ (its columns are this workgroup's alone)
-      const int t = tid >> 2, c4 = (tid & 3) * 4;
+    if (tid < 256 * CB) {   // U replaces U~ (its columns are this workgroup's alone)
+      const int t = (tid >> 2) & (C - 1), c4 = 4 * (tid & 3) + 16 * (tid >> 8);
       const float *s0p = &sUt[p][0][c4 * LU + t], *s1p = &sUt[p][1][c4 * LU + t];
       *reinterpret_cast<float4 *>(rec + R_UT + cblk(t, c0 + c4, C)) =
           make_float4(s0p[0] + s1p[0], s0p[LU] + s1p[LU], s0p[2 * LU] + s1p[2 * LU], s0p[3 * LU] + s1p[3 * LU]);
     }
     // S = D S + K_dec^T U, rows 16w..
-    const float *bu0 = &sUt[p][0][r * LU + 4 * q], *bu1 = &sUt[p][1][r * LU + 4 * q];
-    f32x4 s0, s1 = zero4();
-    s0[0] = Bf.d.x * S[0];
-    s0[1] = Bf.d.y * S[1];
-    s0[2] = Bf.d.z * S[2];
-    s0[3] = Bf.d.w * S[3];
 #pragma unroll
-    for (int kb = 0; kb < 4; kb += 2) {
-      const float4 x0 = ld4(bu0 + 16 * kb), y0 = ld4(bu1 + 16 * kb);
-      const float4 x1 = ld4(bu0 + 16 * kb + 16), y1 = ld4(bu1 + 16 * kb + 16);
-      s0 = mma16(s0, Bf.kd[kb], make_float4(x0.x + y0.x, x0.y + y0.y, x0.z + y0.z, x0.w + y0.w));
-      s1 = mma16(s1, Bf.kd[kb + 1], make_float4(x1.x + y1.x, x1.y + y1.y, x1.z + y1.z, x1.w + y1.w));
+    for (int j = 0; j < CB; ++j) {
+      const float *bu0 = &sUt[p][0][(16 * j + r) * LU + 4 * q], *bu1 = &sUt[p][1][(16 * j + r) * LU + 4 * q];
+      f32x4 s0, s1 = zero4();
+      s0[0] = Bf.d.x * S[j][0];
+      s0[1] = Bf.d.y * S[j][1];
+      s0[2] = Bf.d.z * S[j][2];
+      s0[3] = Bf.d.w * S[j][3];
+#pragma unroll
+      for (int kb = 0; kb < 4; kb += 2) {
+        const float4 x0 = ld4(bu0 + 16 * kb), y0 = ld4(bu1 + 16 * kb);
+        const float4 x1 = ld4(bu0 + 16 * kb + 16), y1 = ld4(bu1 + 16 * kb + 16);
+        s0 = mma16(s0, Bf.kd[kb], make_float4(x0.x + y0.x, x0.y + y0.y, x0.z + y0.z, x0.w + y0.w));
+        s1 = mma16(s1, Bf.kd[kb + 1], make_float4(x1.x + y1.x, x1.y + y1.y, x1.z + y1.z, x1.w + y1.w));
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[j][e] = s0[e] + s1[e];
+      *reinterpret_cast<float4 *>(&sSt[p ^ 1][(16 * j + r) * LT + 16 * w + 4 * q]) =
+          make_float4(S[j][0], S[j][1], S[j][2], S[j][3]);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) S[e] = s0[e] + s1[e];
-    *reinterpret_cast<float4 *>(&sSt[p ^ 1][r * LT + 16 * w + 4 * q]) = make_float4(S[0], S[1], S[2], S[3]);
     loadB(Bf, cn);
     {   // the state entering this chunk, rows of 16 columns from its LDS copy (unchanged
         // this step).  Issued after the prefetches: the wait counter completes in issue
         // order, so no wait for a prefetched fragment also waits for this store.
       float *sin = a.sin + (static_cast<size_t>(bh) * a.NC + c) * D * D;
-      const int i = tid >> 2, c4 = (tid & 3) * 4;
-      const float *src = &sSt[p][c4 * LT + i];
-      *reinterpret_cast<float4 *>(sin + cblk(i, c0 + c4, D)) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
+#pragma unroll
+      for (int x = 0; x < CB; ++x) {
+        const int i = tid >> 2, c4 = 4 * (tid & 3) + 16 * x;
+        const float *src = &sSt[p][c4 * LT + i];
+        *reinterpret_cast<float4 *>(sin + cblk(i, c0 + c4, D)) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
+      }
     }
     lds_barrier();
   }
@@ -455,16 +475,18 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void b
 struct RevA { float4 f[6]; float4 d; };
 struct RevB { float4 qt[4]; float4 wt[4]; };
 
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void bwd_rev(BwdArgs a) {
-  __shared__ __align__(16) float sdSt[2][16 * LT];
-  __shared__ __align__(16) float sdOt[2][16 * LU];
-  __shared__ __align__(16) float sdUt[2][2][16 * LU];
+template <int CB>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4 / CB))) void bwd_rev(BwdArgs a) {
+  constexpr int NU = 8 / CB, NCOL = 16 * CB;
+  __shared__ __align__(16) float sdSt[2][NCOL * LT];
+  __shared__ __align__(16) float sdOt[2][NCOL * LU];
+  __shared__ __align__(16) float sdUt[2][2][NCOL * LU];
   int bh, cb;
-  if (!sweep_unit(a.B * a.H, bh, cb)) return;
+  if (!sweep_unit<NU>(a.B * a.H, bh, cb)) return;
   const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, q = lane >> 4;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ta = w & 3, kh = w >> 2;
-  const int c0 = 16 * cb, b = bh / a.H, h = bh % a.H;
+  const int c0 = NCOL * cb, b = bh / a.H, h = bh % a.H;
   const float *recs = a.rec + static_cast<size_t>(bh) * a.NC * REC;
   // contraction blocks of dU: kh = 0 takes P^T blocks 0..3 (over t) and K_dec blocks 0..1
   // (over i); kh = 1 takes K_dec blocks 2..7
@@ -489,9 +511,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void b
       x.wt[kb] = col4(rec + R_W + (16 * kb + 4 * q) * D + 16 * w + r, D);
     }
   };
-  // one float4 of a chunk's dO block [64][16] for each of the first 256 threads (rows
-  // past the end read 0), stored transposed
-  const int ot = (tid & 255) >> 2, ox = (tid & 3) * 4;
+  // one float4 of a chunk's dO block [64][16 CB] for each of the first 256 CB threads
+  // (rows past the end read 0), stored transposed; the other threads (CB = 1) load a
+  // duplicate inside the unit's columns and store nothing
+  const int ot = (tid >> 2) & (C - 1), ox = 4 * (tid & 3) + 16 * ((tid >> 8) & (CB - 1));
   auto loadO = [&](int c) {
     const int t = c * C + ot;
     float4 v = ld4(a.dO + tok_off(a, b, h, min(t, a.T - 1)) + c0 + ox);
@@ -499,18 +522,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void b
     return v;
   };
   auto storeO = [&](float *dst, float4 v) {
-    if (tid < 256) {
+    if (tid < 256 * CB) {
       dst[(ox + 0) * LU + ot] = v.x;
       dst[(ox + 1) * LU + ot] = v.y;
       dst[(ox + 2) * LU + ot] = v.z;
       dst[(ox + 3) * LU + ot] = v.w;
     }
   };
-  f32x4 dS;
+  f32x4 dS[CB];
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
-    dS[e] = a.dSf ? a.dSf[(static_cast<size_t>(bh) * D + 16 * w + 4 * q + e) * D + c0 + r] : 0.f;
-  *reinterpret_cast<float4 *>(&sdSt[0][r * LT + 16 * w + 4 * q]) = make_float4(dS[0], dS[1], dS[2], dS[3]);
+  for (int j = 0; j < CB; ++j) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      dS[j][e] = a.dSf ? a.dSf[(static_cast<size_t>(bh) * D + 16 * w + 4 * q + e) * D + c0 + 16 * j + r] : 0.f;
+    *reinterpret_cast<float4 *>(&sdSt[0][(16 * j + r) * LT + 16 * w + 4 * q]) =
+        make_float4(dS[j][0], dS[j][1], dS[j][2], dS[j][3]);
+  }
   if (a.NC > 0) {
     RevA A;
     RevB Bf;
@@ -522,68 +549,80 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void b
       const int cn = max(c - 1, 0);   // the last step reloads its own chunk
       const float4 ov = loadO(cn);
       // partial dU over this wave's six contraction blocks
-      f32x4 u0 = zero4(), u1 = zero4();
-      if (kh == 0) {
-        const float *bo = &sdOt[p][r * LU + 4 * q], *bs = &sdSt[p][r * LT + 4 * q];
-        u0 = mma16(u0, A.f[0], ld4(bo));
-        u1 = mma16(u1, A.f[1], ld4(bo + 16));
-        u0 = mma16(u0, A.f[2], ld4(bo + 32));
-        u1 = mma16(u1, A.f[3], ld4(bo + 48));
-        u0 = mma16(u0, A.f[4], ld4(bs));
-        u1 = mma16(u1, A.f[5], ld4(bs + 16));
-      } else {
-        const float *bs = &sdSt[p][r * LT + 32 + 4 * q];
 #pragma unroll
-        for (int j = 0; j < 6; j += 2) {
-          u0 = mma16(u0, A.f[j], ld4(bs + 16 * j));
-          u1 = mma16(u1, A.f[j + 1], ld4(bs + 16 * j + 16));
+      for (int j = 0; j < CB; ++j) {
+        f32x4 u0 = zero4(), u1 = zero4();
+        if (kh == 0) {
+          const float *bo = &sdOt[p][(16 * j + r) * LU + 4 * q], *bs = &sdSt[p][(16 * j + r) * LT + 4 * q];
+          u0 = mma16(u0, A.f[0], ld4(bo));
+          u1 = mma16(u1, A.f[1], ld4(bo + 16));
+          u0 = mma16(u0, A.f[2], ld4(bo + 32));
+          u1 = mma16(u1, A.f[3], ld4(bo + 48));
+          u0 = mma16(u0, A.f[4], ld4(bs));
+          u1 = mma16(u1, A.f[5], ld4(bs + 16));
+        } else {
+          const float *bs = &sdSt[p][(16 * j + r) * LT + 32 + 4 * q];
+#pragma unroll
+          for (int x = 0; x < 6; x += 2) {
+            u0 = mma16(u0, A.f[x], ld4(bs + 16 * x));
+            u1 = mma16(u1, A.f[x + 1], ld4(bs + 16 * x + 16));
+          }
         }
+        *reinterpret_cast<float4 *>(&sdUt[p][kh][(16 * j + r) * LU + 16 * ta + 4 * q]) =
+            make_float4(u0[0] + u1[0], u0[1] + u1[1], u0[2] + u1[2], u0[3] + u1[3]);
       }
-      *reinterpret_cast<float4 *>(&sdUt[p][kh][r * LU + 16 * ta + 4 * q]) =
-          make_float4(u0[0] + u1[0], u0[1] + u1[1], u0[2] + u1[2], u0[3] + u1[3]);
       const float4 dcur = A.d;
       loadA(A, cn);
       lds_barrier();
-      if (tid < 256) {   // dU rows from the LDS partial sums
+      if (tid < 256 * CB) {   // dU rows from the LDS partial sums
         float *du = a.du + (static_cast<size_t>(bh) * a.NC + c) * C * D;
-        const int t = tid >> 2, c4 = (tid & 3) * 4;
+        const int t = (tid >> 2) & (C - 1), c4 = 4 * (tid & 3) + 16 * (tid >> 8);
         const float *s0p = &sdUt[p][0][c4 * LU + t], *s1p = &sdUt[p][1][c4 * LU + t];
         *reinterpret_cast<float4 *>(du + cblk(t, c0 + c4, C)) =
             make_float4(s0p[0] + s1p[0], s0p[LU] + s1p[LU], s0p[2 * LU] + s1p[2 * LU], s0p[3 * LU] + s1p[3 * LU]);
       }
       // dS = D dS + Q~^T dO - W^T dU, rows 16w..
-      const float *bo = &sdOt[p][r * LU + 4 * q];
-      const float *bu0 = &sdUt[p][0][r * LU + 4 * q], *bu1 = &sdUt[p][1][r * LU + 4 * q];
-      f32x4 s0, s1 = zero4();
-      s0[0] = dcur.x * dS[0];
-      s0[1] = dcur.y * dS[1];
-      s0[2] = dcur.z * dS[2];
-      s0[3] = dcur.w * dS[3];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const float4 x = ld4(bu0 + 16 * kb), y = ld4(bu1 + 16 * kb);
-        s0 = mma16(s0, Bf.qt[kb], ld4(bo + 16 * kb));
-        s1 = mma16(s1, Bf.wt[kb], make_float4(-(x.x + y.x), -(x.y + y.y), -(x.z + y.z), -(x.w + y.w)));
+      for (int j = 0; j < CB; ++j) {
+        const float *bo = &sdOt[p][(16 * j + r) * LU + 4 * q];
+        const float *bu0 = &sdUt[p][0][(16 * j + r) * LU + 4 * q], *bu1 = &sdUt[p][1][(16 * j + r) * LU + 4 * q];
+        f32x4 s0, s1 = zero4();
+        s0[0] = dcur.x * dS[j][0];
+        s0[1] = dcur.y * dS[j][1];
+        s0[2] = dcur.z * dS[j][2];
+        s0[3] = dcur.w * dS[j][3];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const float4 x = ld4(bu0 + 16 * kb), y = ld4(bu1 + 16 * kb);
+          s0 = mma16(s0, Bf.qt[kb], ld4(bo + 16 * kb));
+          s1 = mma16(s1, Bf.wt[kb], make_float4(-(x.x + y.x), -(x.y + y.y), -(x.z + y.z), -(x.w + y.w)));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dS[j][e] = s0[e] + s1[e];
+        *reinterpret_cast<float4 *>(&sdSt[p ^ 1][(16 * j + r) * LT + 16 * w + 4 * q]) =
+            make_float4(dS[j][0], dS[j][1], dS[j][2], dS[j][3]);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) dS[e] = s0[e] + s1[e];
-      *reinterpret_cast<float4 *>(&sdSt[p ^ 1][r * LT + 16 * w + 4 * q]) = make_float4(dS[0], dS[1], dS[2], dS[3]);
       storeO(sdOt[p ^ 1], ov);
       loadB(Bf, cn);
       {   // dS after this chunk (unchanged this step), after the prefetches as in the
           // state sweep
         float *dsa = a.dsa + (static_cast<size_t>(bh) * a.NC + c) * D * D;
-        const int i = tid >> 2, c4 = (tid & 3) * 4;
-        const float *src = &sdSt[p][c4 * LT + i];
-        *reinterpret_cast<float4 *>(dsa + cblk(i, c0 + c4, D)) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
+#pragma unroll
+        for (int x = 0; x < CB; ++x) {
+          const int i = tid >> 2, c4 = 4 * (tid & 3) + 16 * x;
+          const float *src = &sdSt[p][c4 * LT + i];
+          *reinterpret_cast<float4 *>(dsa + cblk(i, c0 + c4, D)) = make_float4(src[0], src[LT], src[2 * LT], src[3 * LT]);
+        }
       }
       lds_barrier();
     }
   }
   if (a.dS0)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      a.dS0[(static_cast<size_t>(bh) * D + 16 * w + 4 * q + e) * D + c0 + r] = dS[e];
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        a.dS0[(static_cast<size_t>(bh) * D + 16 * w + 4 * q + e) * D + c0 + 16 * j + r] = dS[j][e];
 }
 
 // ---------------------------------------------------------------------------
@@ -1034,13 +1073,13 @@ hipError_t launch_backward(const kda_backward_desc &d, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const unsigned sweep_grid = static_cast<unsigned>((BH + 7) / 8 * 64);
+  const unsigned sweep_grid = static_cast<unsigned>((BH + 7) / 8 * 8 * (8 / SWEEP_CB));
   if (nch > 0) {
-    bwd_fwd<<<dim3(sweep_grid), dim3(512), 0, s>>>(a);
+    bwd_fwd<SWEEP_CB><<<dim3(sweep_grid), dim3(512), 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  bwd_rev<<<dim3(sweep_grid), dim3(512), 0, s>>>(a);
+  bwd_rev<SWEEP_CB><<<dim3(sweep_grid), dim3(512), 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nch > 0) {
