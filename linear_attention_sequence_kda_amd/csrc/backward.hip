@@ -17,14 +17,15 @@
 // and the pairwise terms of dKK and dP into dk, dq and dG, the elementwise terms of
 // Q~, k e^G and K_dec, then dg_u = [-5 <= g_u <= 0] (sum_{t >= u} dG_t + dGam).
 //
-// Pairwise decays e^{G_t - G_j} are factored through the first token of a 16-token block
-// (block start R): for t >= R >= ... each factor stays inside fp32 range because every
-// step's log-decay is at least -5 (15 steps in a block: at most e^75), the same bound the
-// forward's 16-token diagonal tiles rely on.
+// Pairwise decays e^{G_t - G_j} (j <= t) are factored through the first token R of a
+// 16-token block: e^{G_t - G_R} e^{G_R - G_j}, with R the start of j's block or of t's
+// block.  Each factor stays inside fp32 range because every step's log-decay is at least
+// -5 (15 steps within a block: at most e^75), the bound the forward's 16-token diagonal
+// tiles rely on; a factor that underflows multiplies a term below fp32 resolution.
 //
 // Four kernels:
-//   bwd_prep    one workgroup per chunk: G, K_dec, Q~, P, KK, M, W, U~, D -> record
-//   bwd_fwd     per (sequence, head, 16 value columns): states entering every chunk, U
+//   bwd_prep    one workgroup per chunk: G, K_dec, Q~, P^T, KK, M, W, U~, D -> record
+//   bwd_fwd     per (sequence, head, 32 value columns): states entering every chunk, U
 //   bwd_rev     same split, reverse order: dS after every chunk, dU, and dS0
 //   bwd_grad    one workgroup per chunk: dq, dk, dv, dg, dbeta of the chunk's tokens
 #include "internal.h"
@@ -37,7 +38,6 @@ constexpr int D = 128;        // d_k = d_v
 constexpr int C = 64;         // tokens per chunk
 constexpr int LD = D + 4;     // LDS row stride of [C][D] tiles
 constexpr int LS = C + 4;     // LDS row stride of [C][C] tiles
-constexpr int LV = 20;        // LDS row stride of [*][16] column blocks
 
 // per-chunk record, floats.  P is kept transposed (the chunk kernel's MFMA output
 // fragments hold four consecutive rows of it, the gradient sweep reads its columns).
@@ -77,7 +77,6 @@ __device__ __forceinline__ float4 ld4(const float *p) { return *reinterpret_cast
 __device__ __forceinline__ float4 col4(const float *p, int ld) {
   return make_float4(p[0], p[ld], p[2 * ld], p[3 * ld]);
 }
-__device__ __forceinline__ float4 neg4(float4 x) { return make_float4(-x.x, -x.y, -x.z, -x.w); }
 __device__ __forceinline__ float4 mul4(float4 a, float4 b) {
   return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
 }
@@ -91,7 +90,7 @@ __device__ __forceinline__ int cblk(int row, int col, int rows) {
   return (col >> 4) * rows * 16 + row * 16 + (col & 15);
 }
 
-// element offset of token t of chunk c in a [B,T,H,D] array
+// element offset of token t of a [B,T,H,D] array, head h
 __device__ __forceinline__ size_t tok_off(const BwdArgs &a, int b, int h, int t) {
   return (static_cast<size_t>(b) * a.T + t) * a.H * D + static_cast<size_t>(h) * D;
 }
