@@ -354,7 +354,6 @@ __device__ __forceinline__ bool sweep_unit(int BH, int &bh, int &cb) {
 // rows go to global memory as 16-byte stores from those copies.
 constexpr int LT = D + 4;   // row stride of a transposed [16][D] block
 constexpr int LU = C + 4;   // row stride of a transposed [16][C] block
-constexpr int SWEEP_CB = 2; // 16-column blocks per sweep unit
 
 template <int CB> struct FwdA { float4 w[4]; float ut[CB][4]; };
 struct FwdB { float4 kd[4]; float4 d; };
@@ -1072,13 +1071,24 @@ hipError_t launch_backward(const kda_backward_desc &d, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const unsigned sweep_grid = static_cast<unsigned>((BH + 7) / 8 * 8 * (8 / SWEEP_CB));
+  // Sweep units of 32 columns (each record fragment a wave loads serves two column
+  // blocks) when there are enough of them to give every CU one; with few (sequence,
+  // head) pairs, as in a long single sequence, units of 16 columns double the parallelism.
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ncu = v;
+  }
+  const bool wide = static_cast<int64_t>(BH) * 4 >= ncu;
+  const unsigned sweep_grid = static_cast<unsigned>((BH + 7) / 8 * 8 * (wide ? 4 : 8));
   if (nch > 0) {
-    bwd_fwd<SWEEP_CB><<<dim3(sweep_grid), dim3(512), 0, s>>>(a);
+    if (wide) bwd_fwd<2><<<dim3(sweep_grid), dim3(512), 0, s>>>(a);
+    else bwd_fwd<1><<<dim3(sweep_grid), dim3(512), 0, s>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  bwd_rev<SWEEP_CB><<<dim3(sweep_grid), dim3(512), 0, s>>>(a);
+  if (wide) bwd_rev<2><<<dim3(sweep_grid), dim3(512), 0, s>>>(a);
+  else bwd_rev<1><<<dim3(sweep_grid), dim3(512), 0, s>>>(a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (nch > 0) {

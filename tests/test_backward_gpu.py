@@ -187,3 +187,11 @@ def test_backward_beta_zero_many_sequences():
         assert e <= TOL, n
     assert err_S(got["dS0"], ref["dS0"]) <= TOL_S
     assert np.abs(got["dk"]).max() <= 1e-6 * np.abs(ref["dq"]).max()
+
+
+def test_backward_wide_sweep_units():
+    """64 (sequence, head) pairs: enough for the sweeps' 32-column units (the smaller cases
+    above run 16-column units); every gradient against the oracle, ragged tail."""
+    c = make_prefill(4, 130, 16, 128, seed=40, in_dtype=BF16, s0_std=0.05)
+    dO, dS = make_output_grads(4, 130, 16, seed=40)
+    check(c, dO, dS, "64 heads x sequences, T=130")
