@@ -193,11 +193,15 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
   constexpr int VS = (MODE == MODE_TRANSITION ? 2 * D : D) / NC;   // workgroups per unit
   // KiB of the record this pass copies (the state map needs only its prefix)
   constexpr int NBLK = (int)((MODE == MODE_TRANSITION ? R::trans : R::bytes) / 1024);
-  // Records, values and norm partials are double buffered (chunks alternate), each
-  // buffer a separate LDS object, so the compiler sees that reads of one buffer do not
-  // depend on the asynchronous copy in flight into the other.
+  // Values and norm partials are double buffered (chunks alternate), records double
+  // buffered for outputs and triple buffered for state maps (the copy of chunk n+2 is
+  // in flight during chunk n: a map step has less work to hide it behind).  Each
+  // buffer is a separate LDS object, so the compiler sees that reads of one buffer do
+  // not depend on the asynchronous copy in flight into another.
+  constexpr int NRB = MODE == MODE_TRANSITION ? 3 : 2;
   __shared__ __align__(16) unsigned char recA[NBLK * 1024];
   __shared__ __align__(16) unsigned char recB[NBLK * 1024];
+  __shared__ __align__(16) unsigned char recC[NRB == 3 ? NBLK * 1024 : 16];
   __shared__ __align__(16) T sVA[KC * VC];             // V [t][c] (rows >= C zero)
   __shared__ __align__(16) T sVB[KC * VC];
   __shared__ __align__(16) float sNormA[GATE ? C * NW : 1];   // per-token, per-wave sums of squares
@@ -319,7 +323,12 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
   {
     const int n1 = min(ch_begin + 1, ch_last);
     load_v<C, NC, F32, MODE>(vr, a, tok_base(n1), min(C, a.T - n1 * C), c0, tid);
+    if constexpr (NRB == 3) copy_rec(recB, n1, 0, NCOPY);
   }
+  // With three record buffers, every memory operation but the record copy issued last
+  // (two buffers ahead) has to be complete at the top of a step.  The count is exact:
+  // every wave issues NCOPY copies per step, after its value loads.
+  static_assert(NRB == 2 || NCOPY < 16, "vmcnt field");
 
   // per-head RMSNorm over the 128 value columns, then the sigmoid gate, applied to the
   // raw outputs op of one chunk, with that chunk's sums of squares and gate logits
@@ -379,15 +388,30 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
     }
   };
 
-  // one chunk, reading record and value buffers BUF (A or B) and filling the others
-  auto step = [&](auto bufc, int chunk) __attribute__((always_inline)) {
+  // one chunk, reading record buffer RB and value buffer BUF (A or B) and filling the
+  // others: the record copy goes to the buffer NRB - 1 ahead
+  auto recbuf = [&](int i) __attribute__((always_inline)) { return i == 0 ? recA : i == 1 ? recB : recC; };
+  auto step = [&](auto bufc, auto rbc, int chunk) __attribute__((always_inline)) {
     constexpr int BUF = decltype(bufc)::value;
-    unsigned char *rc = BUF == 0 ? recA : recB;
-    unsigned char *rn = BUF == 0 ? recB : recA;
+    constexpr int RB = decltype(rbc)::value;
+    unsigned char *rc = recbuf(RB);
+    unsigned char *rn = recbuf((RB + NRB - 1) % NRB);
     const T *sV = BUF == 0 ? sVA : sVB;
     T *sVn = BUF == 0 ? sVB : sVA;
-    __builtin_amdgcn_s_waitcnt(0x0F70);                // vmcnt(0): this wave's loads landed
-    __syncthreads();                                   // every wave's; V of this chunk visible
+    if constexpr (NRB == 2) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0): this wave's loads landed
+      __syncthreads();                                 // every wave's; V of this chunk visible
+    } else {
+      // The same with the record copy issued last still in flight, and a barrier without
+      // a memory fence (a fence would wait for it): every exchange through LDS is
+      // complete once lgkmcnt and vmcnt have counted it.  Nothing of the step moves above
+      // the barrier, where a use of the value registers would again wait for everything.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0x0070 | NCOPY);      // vmcnt(NCOPY) lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     const bool prev = MODE == MODE_OUTPUT && chunk > ch_begin;
     if constexpr (GATE) {
@@ -410,21 +434,17 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
     auto fetch = [&](int i) __attribute__((always_inline)) {
       return Op<F32>::load(reinterpret_cast<const T *>(rc + SF::seq.off[i] + lane * 8 * sizeof(T)));
     };
-    // The next chunk's record copy.  While an asynchronous copy into LDS is in flight
-    // the compiler waits for all outstanding LDS reads at every use, which defeats the
-    // read-ahead, so the outputs pass issues it after its last fragment read; the state
-    // map pass has less work after that point and issues it first.
-    if constexpr (MODE == MODE_TRANSITION) {
-      copy_rec(rn, nx, 0, NCOPY);
-      __builtin_amdgcn_sched_barrier(0);
-    }
     V8 ring[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) ring[i] = fetch(i);
+    // A later record's copy is issued after the step's last fragment read: while an
+    // asynchronous copy into LDS is in flight the compiler waits for all outstanding LDS
+    // reads at every use, which defeats the read-ahead.  The outputs pass copies the
+    // next chunk's record, the state map pass (three buffers) the one after it.
     auto take = [&](int i) __attribute__((always_inline)) {
       const V8 f = ring[i % PF];
       if (i + PF < SF::n) ring[i % PF] = fetch(i + PF);
-      if (MODE == MODE_OUTPUT && i + PF == SF::n - 1) copy_rec(rn, nx, 0, NCOPY);
+      if (i + PF == SF::n - 1) copy_rec(rn, NRB == 2 ? nx : min(chunk + 2, ch_last), 0, NCOPY);
       __builtin_amdgcn_sched_barrier(0);             // keep the read PF products ahead
       return f;
     };
@@ -547,9 +567,31 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
       }
     }
   };
-  for (int chunk = ch_begin; chunk < ch_end; chunk += 2) {
-    step(std::integral_constant<int, 0>{}, chunk);
-    if (chunk + 1 < ch_end) step(std::integral_constant<int, 1>{}, chunk + 1);
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  if constexpr (NRB == 2) {
+    for (int chunk = ch_begin; chunk < ch_end; chunk += 2) {
+      step(I0{}, I0{}, chunk);
+      if (chunk + 1 < ch_end) step(I1{}, I1{}, chunk + 1);
+    }
+  } else {
+    // (the loop is left as soon as the chunks run out, so that no path skips a step and
+    // runs a later one: the compiler's wait counts stay exact at every step)
+    for (int chunk = ch_begin;; chunk += 6) {
+      step(I0{}, I0{}, chunk);
+      if (chunk + 1 >= ch_end) break;
+      step(I1{}, I1{}, chunk + 1);
+      if (chunk + 2 >= ch_end) break;
+      step(I0{}, I2{}, chunk + 2);
+      if (chunk + 3 >= ch_end) break;
+      step(I1{}, I0{}, chunk + 3);
+      if (chunk + 4 >= ch_end) break;
+      step(I0{}, I1{}, chunk + 4);
+      if (chunk + 5 >= ch_end) break;
+      step(I1{}, I2{}, chunk + 5);
+      if (chunk + 6 >= ch_end) break;
+    }
   }
   if constexpr (MODE == MODE_OUTPUT) {
     __builtin_amdgcn_s_waitcnt(0x0F70);                // gate of the last chunk
