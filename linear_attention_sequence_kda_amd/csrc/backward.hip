@@ -28,6 +28,8 @@
 //   bwd_fwd     per (sequence, head, 32 value columns): states entering every chunk, U
 //   bwd_rev     same split, reverse order: dS after every chunk, dU, and dS0
 //   bwd_grad    one workgroup per chunk: dq, dk, dv, dg, dbeta of the chunk's tokens
+#include <type_traits>
+
 #include "internal.h"
 #include "kda_device.h"
 
@@ -126,13 +128,37 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
   const int t0 = c * C, Tc = min(C, a.T - t0);
   float *rec = a.rec + static_cast<size_t>(ch) * REC;
 
-  // decays (log2 units) and beta; tokens past the sequence end are zero
+  // Every input of the chunk is loaded here, so that the k, q and v loads overlap the
+  // decay scan; k, q and v stay in their input format until used.
+  using Raw4 = typename std::conditional<BF16, uint2, float4>::type;
+  Raw4 kraw[4], qraw[4], vraw[4];
+  auto widen = [](const Raw4 &x) __attribute__((always_inline)) {
+    if constexpr (BF16) {
+      return make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xffff0000u),
+                         __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xffff0000u));
+    } else {
+      return x;
+    }
+  };
+  // decays (log2 units) and beta; tokens past the sequence end are zero.  beta and g
+  // are loaded first: the in-order wait counter then lets their first use proceed while
+  // k, q and v are still in flight.
+  const float beta_t = tid < Tc ? a.beta[(static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h] : 0.f;
   {
     float4 gv[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
       gv[x] = ld4(a.g + tok_off(a, b, h, t0 + min(t, Tc - 1)) + i);
+    }
+    using E = typename std::conditional<BF16, uint16_t, float>::type;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
+      const size_t o = tok_off(a, b, h, t0 + min(t, Tc - 1)) + i;
+      kraw[x] = *reinterpret_cast<const Raw4 *>(static_cast<const E *>(a.k) + o);
+      qraw[x] = *reinterpret_cast<const Raw4 *>(static_cast<const E *>(a.q) + o);
+      vraw[x] = *reinterpret_cast<const Raw4 *>(static_cast<const E *>(a.v) + o);
     }
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
@@ -143,11 +169,22 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
     }
   }
   for (int e = tid; e < C * LS; e += 512) { sA[e] = 0.f; sM[e] = 0.f; }
-  if (tid < C) sBeta[tid] = tid < Tc ? a.beta[(static_cast<size_t>(b) * a.T + t0 + tid) * a.H + h] : 0.f;
+  if (tid < C) sBeta[tid] = beta_t;
   lds_barrier();
-  if (tid < D) {
+  {   // inclusive scan over the chunk: four 16-token parts per channel, then offsets
+    float *sTot = &sZ[0][0];   // part totals [4][D] (sZ is free until the solve)
+    const int i = tid & (D - 1), part = tid >> 7;
     float s = 0.f;
-    for (int t = 0; t < C; ++t) { s += sG[t * LD + tid]; sG[t * LD + tid] = s; }
+#pragma unroll
+    for (int t = 16 * part; t < 16 * part + 16; ++t) { s += sG[t * LD + i]; sG[t * LD + i] = s; }
+    sTot[part * D + i] = s;
+    lds_barrier();
+    float off = 0.f;
+    for (int p = 0; p < part; ++p) off += sTot[p * D + i];
+    if (part > 0) {
+#pragma unroll
+      for (int t = 16 * part; t < 16 * part + 16; ++t) sG[t * LD + i] += off;
+    }
   }
   lds_barrier();
   if (tid < D) {
@@ -164,10 +201,8 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
   float4 kv[4], qv[4];
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
-    const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
-    const size_t o = tok_off(a, b, h, t0 + min(t, Tc - 1)) + i;
-    kv[x] = load4<BF16>(a.k, o);
-    qv[x] = load4<BF16>(a.q, o);
+    kv[x] = widen(kraw[x]);
+    qv[x] = widen(qraw[x]);
   }
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
@@ -291,10 +326,7 @@ __global__ __launch_bounds__(512, 1) void bwd_prep(BwdArgs a) {
   {
     float4 vv[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
-      vv[x] = load4<BF16>(a.v, tok_off(a, b, h, t0 + min(t, Tc - 1)) + i);
-    }
+    for (int x = 0; x < 4; ++x) vv[x] = widen(vraw[x]);
 #pragma unroll
     for (int x = 0; x < 4; ++x) {
       const int e = tid + 512 * x, t = e >> 5, i = (e & 31) * 4;
