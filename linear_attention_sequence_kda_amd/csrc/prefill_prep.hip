@@ -83,6 +83,7 @@ struct RawPrep {
                         // g[2kb + 1] channels 32kb + 16 + 4lg + (0..3)
   Q8<F32> k[4], q[4];
   float beta;
+  bool ok;              // the lane's token lies in the sequence (else its inputs read as 0)
 };
 
 // Global loads of one chunk, zero-filled past the sequence end.  Wave w < NT loads
@@ -98,22 +99,34 @@ __device__ __forceinline__ void load_prep(RawPrep<F32> &r, const PrepArgs &a, in
   const int t0 = chunk * C;
   const int tt = 16 * wave + lr;
   const bool ok = wave < NT && t0 + tt < a.T;
-  const size_t tok = (size_t)b * a.T + t0 + tt;
+  // Lanes past the sequence end (or of waves without a tile) load the chunk's first
+  // token instead and use zeros, so the loads are branch-free.  They are issued in the
+  // order of first use (beta and g in the decay scan, then k and q): the wait counter
+  // completes in issue order, so the scan does not wait for k and q.
+  const size_t tok = (size_t)b * a.T + t0 + (ok ? tt : 0);
   const size_t base = (tok * a.H + h) * D + 4 * lg;
+  r.ok = ok;
+  r.beta = a.beta[tok * a.H + h];
 #pragma unroll
   for (int kb = 0; kb < 4; ++kb) {
-    if (ok) {
-      r.g[2 * kb] = *reinterpret_cast<const float4 *>(a.g + base + 32 * kb);
-      r.g[2 * kb + 1] = *reinterpret_cast<const float4 *>(a.g + base + 32 * kb + 16);
-      r.k[kb] = load_q8_split<F32>(a.k, base + 32 * kb);
-      r.q[kb] = load_q8_split<F32>(a.q, base + 32 * kb);
-    } else {
-      r.g[2 * kb] = r.g[2 * kb + 1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      r.k[kb] = zero_q8<F32>();
-      r.q[kb] = zero_q8<F32>();
-    }
+    r.g[2 * kb] = *reinterpret_cast<const float4 *>(a.g + base + 32 * kb);
+    r.g[2 * kb + 1] = *reinterpret_cast<const float4 *>(a.g + base + 32 * kb + 16);
   }
-  r.beta = ok ? a.beta[tok * a.H + h] : 0.f;
+  __builtin_amdgcn_sched_barrier(0);   // keep this order
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) r.k[kb] = load_q8_split<F32>(a.k, base + 32 * kb);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) r.q[kb] = load_q8_split<F32>(a.q, base + 32 * kb);
+}
+
+// Workgroup barrier for LDS only: waits for this wave's LDS accesses, not for its global
+// loads, so that loads issued earlier stay in flight across it (the kernel never reads
+// global memory it writes).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // one step of the 16-lane inclusive scan on 8 independent values (DPP row shift right)
@@ -198,6 +211,8 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : (C == 64 ? 4 : 2)) void chunk_p
         float gg[8];
         f8_from(gg, raw.g[2 * kb], raw.g[2 * kb + 1]);
 #pragma unroll
+        for (int e = 0; e < 8; ++e) gg[e] = raw.ok ? gg[e] : 0.f;
+#pragma unroll
         for (int e = 0; e < 8; ++e) Lc[8 * kb + e] = log2_decay(gg[e]);
         scan_step<0x111>(Lc + 8 * kb);
         scan_step<0x112>(Lc + 8 * kb);
@@ -212,9 +227,9 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : (C == 64 ? 4 : 2)) void chunk_p
           *reinterpret_cast<float4 *>(pp + 16) = make_float4(dp[4], dp[5], dp[6], dp[7]);
         }
       }
-      if (lg == 0) sBeta[tt] = raw.beta;
+      if (lg == 0) sBeta[tt] = raw.ok ? raw.beta : 0.f;
     }
-    __syncthreads();
+    lds_barrier();   // k and q may still be in flight
 
     // ===== per (tile, channel): prefix and suffix decay products, the chunk decay,
     // and the factors between tiles two or more apart =====
@@ -247,7 +262,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : (C == 64 ? 4 : 2)) void chunk_p
     } else {
       if (tid < D) { sPre[tid] = 1.f; sPost[tid] = 1.f; sDecay[tid] = sDpow[tid]; }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ===== A2: decay factors, diagonal tile, chunk-level operands =====
     V8 rkx[4], rqx[4];                                 // k e^{G_t - r_w}, q e^{G_t - r_w}
@@ -271,7 +286,8 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : (C == 64 ? 4 : 2)) void chunk_p
         V8 xq;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float Lv = Lc[8 * kb + e], kk = q8_at<F32>(raw.k[kb], e), qq = q8_at<F32>(raw.q[kb], e);
+          const float Lv = Lc[8 * kb + e];
+          const float kk = raw.ok ? q8_at<F32>(raw.k[kb], e) : 0.f, qq = raw.ok ? q8_at<F32>(raw.q[kb], e) : 0.f;
           const float E = exp2_fast(Lv);               // e^{G_t - r_w}      in [e^-80, 1]
           const float En = exp2_fast(-Lv);             // e^{r_w - G_t}      in [1, e^80]
           rk[e] = kk * E;
@@ -317,7 +333,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : (C == 64 ? 4 : 2)) void chunk_p
         accPd[r] = ti <= lr ? accPd[r] : 0.f;
       }
     }
-    __syncthreads();   // KF, Kt, decay, diagonal A/P visible
+    lds_barrier();   // KF, Kt, decay, diagonal A/P visible
 
     // ===== A3: wave 0 inverts every diagonal block of I + A (one column per lane);
     // waves w >= 1 compute the off-diagonal tiles (w, s'), s' < w, with row operand
@@ -404,7 +420,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : (C == 64 ? 4 : 2)) void chunk_p
       for (int e = 0; e < 8; ++e) v[e] = Op<F32>::cvt(static_cast<float>(v[e]) * (e < 4 ? post0 : post1));
       Op<F32>::store(reinterpret_cast<T *>(out + R::frag(R::oK, f, lane)), v);
     }
-    __syncthreads();   // A, P, diagonal inverses complete; KF dead
+    lds_barrier();   // A, P, diagonal inverses complete; KF dead
     // K e^G = (k e^{G_t - r_w}) prod_{m<w} D_m into KF's storage, for W
     if (wave < NT) {
 #pragma unroll
@@ -420,7 +436,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : (C == 64 ? 4 : 2)) void chunk_p
         st4<F32, D>(sKT, tt, ch + 16, xk[4], xk[5], xk[6], xk[7]);
       }
     }
-    __syncthreads();   // K e^G complete; the per-tile vectors are dead
+    lds_barrier();   // K e^G complete; the per-tile vectors are dead
 
     // ===== solve: wave w walks down column block w of X = (I + A)^-1:
     // X_{s,w} = -X_ss sum_{w<=m<s} A_{s,m} X_{m,w}; a 16x16 result in MFMA output layout
@@ -470,7 +486,7 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : (C == 64 ? 4 : 2)) void chunk_p
                     on ? xc[s][2] * bj : 0.f, on ? xc[s][3] * bj : 0.f);
       }
     }
-    __syncthreads();   // T complete
+    lds_barrier();   // T complete
 
     // ===== W = T (K e^G): fragment (tb, kb) straight from the two W^T tiles (2kb, tb)
     // and (2kb + 1, tb), each W^T = Kt^T T^T over the chunk's tokens =====

@@ -577,7 +577,8 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
     }
   } else {
     // (the loop is left as soon as the chunks run out, so that no path skips a step and
-    // runs a later one: the compiler's wait counts stay exact at every step)
+    // runs a later one: the compiler's wait counts stay exact at every step; segments are
+    // never empty, so the first step always runs)
     for (int chunk = ch_begin;; chunk += 6) {
       step(I0{}, I0{}, chunk);
       if (chunk + 1 >= ch_end) break;
