@@ -399,8 +399,15 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
     const T *sV = BUF == 0 ? sVA : sVB;
     T *sVn = BUF == 0 ? sVB : sVA;
     if constexpr (NRB == 2) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);              // vmcnt(0): this wave's loads landed
-      __syncthreads();                                 // every wave's; V of this chunk visible
+      // This wave's loads and record copies landed: all but the previous step's output
+      // stores, issued last (NT * CBW of them when that step had outputs to store), then
+      // a barrier without a memory fence (a fence would wait for the stores too).
+      static_assert(NT * CBW < 16, "vmcnt field");
+      asm volatile("" ::: "memory");
+      if (MODE == MODE_OUTPUT && chunk - 1 > ch_begin) __builtin_amdgcn_s_waitcnt(0x0070 | (NT * CBW));
+      else __builtin_amdgcn_s_waitcnt(0x0070);       // vmcnt(0) lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     } else {
       // The same with the record copy issued last still in flight, and a barrier without
       // a memory fence (a fence would wait for it): every exchange through LDS is
@@ -437,14 +444,18 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
     V8 ring[PF];
 #pragma unroll
     for (int i = 0; i < PF; ++i) ring[i] = fetch(i);
-    // A later record's copy is issued after the step's last fragment read: while an
-    // asynchronous copy into LDS is in flight the compiler waits for all outstanding LDS
-    // reads at every use, which defeats the read-ahead.  The outputs pass copies the
-    // next chunk's record, the state map pass (three buffers) the one after it.
+    // A later record's copy is issued late in the step: while an asynchronous copy into
+    // LDS is in flight the compiler waits for all outstanding LDS reads at every use,
+    // which defeats the read-ahead.  The state map pass (three buffers) copies the record
+    // after next once its last fragment read is issued.  The outputs pass copies the
+    // next record once the reads of the state products are issued, before the output
+    // stores of the previous chunk: the next step then waits for the copy with those
+    // stores still in flight.
+    constexpr int COPY_AT = MODE == MODE_OUTPUT ? R::nW + R::nT + R::nK : SF::n - 1;
     auto take = [&](int i) __attribute__((always_inline)) {
       const V8 f = ring[i % PF];
       if (i + PF < SF::n) ring[i % PF] = fetch(i + PF);
-      if (i + PF == SF::n - 1) copy_rec(rn, NRB == 2 ? nx : min(chunk + 2, ch_last), 0, NCOPY);
+      if (i + PF == COPY_AT) copy_rec(rn, NRB == 2 ? nx : min(chunk + 2, ch_last), 0, NCOPY);
       __builtin_amdgcn_sched_barrier(0);             // keep the read PF products ahead
       return f;
     };
