@@ -20,6 +20,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -67,10 +68,15 @@ def decode_alg_bytes(N, H):
 
 
 def _src_hash(*names):
+    """Hash of the kernel sources with comments and blank space removed, so that the
+    committed counter summary stays valid across comment edits but not code edits."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "linear_attention_sequence_kda_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "linear_attention_sequence_kda_amd", "csrc", n), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -15,8 +15,9 @@
 // accumulators and feed the next products straight from registers (the record's
 // operands are stored with the contraction index in the matching split order).  The
 // only data shared by the waves of a workgroup is the chunk's record, which is
-// copied into LDS once per workgroup by asynchronous global->LDS loads, one chunk
-// ahead (two buffers), and the chunk's values V.  All products are fp16 MFMA with
+// copied into LDS once per workgroup by asynchronous global->LDS loads (one chunk ahead
+// into two buffers for outputs, two chunks ahead into three for state maps), and the
+// chunk's values V.  All products are fp16 MFMA with
 // fp32 accumulation (fp32 MFMA for fp32 inputs).  MODE_TRANSITION computes a
 // segment's state map for the associative scan of context parallelism instead of
 // outputs.
