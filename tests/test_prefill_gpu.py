@@ -169,6 +169,16 @@ def test_segments_with_gate(v_split, out_dtype):
           v_split=v_split, gate=True, norm_weight=w, out_dtype=out_dtype)
 
 
+@pytest.mark.parametrize("seg_chunks", [3, 7, 9, 12])
+def test_segment_lengths(seg_chunks):
+    """Map segments of every length modulo 6 (the state map pass runs its chunks six to
+    an unrolled loop iteration and leaves the loop after any of them), ragged tail."""
+    n_seg = 3
+    T = 64 * seg_chunks * (n_seg - 1) + 64 * (seg_chunks - 1) + 23
+    c = make_prefill(1, T, 2, 128, seed=56 + seg_chunks, in_dtype=BF16, s0_std=0.05)
+    check(c, f"segments of {seg_chunks} chunks", chunk=64, n_segments=n_seg)
+
+
 def test_segments_chunk16_gate():
     c = make_prefill(1, 700, 2, 128, seed=55, in_dtype=BF16, s0_std=0.05, gate=True)
     check(c, "segments chunk16 gate", chunk=16, n_segments=4, gate=True, ckpt_every=128)
