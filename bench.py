@@ -120,8 +120,8 @@ def cpu_baseline(c, gate):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -162,21 +162,20 @@ def main():
     def step():
         kda.kda_prefill_chunked(q, k, v, g, beta, workspace=ws, stream=stream, **kw)
 
+    # warm-up calls (the first tens of calls on a fresh GPU run slower while its clocks
+    # ramp up), then K calls back to back between two events on the launch stream
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(a.steps)]
-    torch.cuda.synchronize()
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start = time.perf_counter()
-    for e0, e1 in ev:
-        e0.record(stream)
+    e_start.record(stream)
+    for _ in range(a.steps):
         step()
-        e1.record(stream)
+    e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    durs = sorted(e0.elapsed_time(e1) for e0, e1 in ev)      # ms, per launch
-    ms_mean = float(np.mean(durs))
+    ms_mean = e_start.elapsed_time(e_end) / a.steps           # average call duration
     ms_step = wall * 1e3 / a.steps
     tokens = B * T
     value = tokens / (ms_step * 1e-3)
@@ -218,7 +217,6 @@ def main():
                       "the call",
             "alg_bytes_per_launch": alg_b,
             "kernel_ms_mean": round(kernel_ms, 4),
-            "kernel_ms_median": round(durs[len(durs) // 2], 4),
         },
         "prefill_mfma": {
             "alg_flops_per_launch": alg_f,
@@ -332,7 +330,7 @@ def main():
             kda.kda_prefill_backward(q, k, v, g, beta, dO, S0=S0, dS_final=dSf, workspace=bws,
                                      stream=stream, **grads)
 
-        for _ in range(3):
+        for _ in range(5):
             bstep()
         torch.cuda.synchronize()
         nb = 10
