@@ -129,7 +129,8 @@ KDA_API kda_status kda_prefill_workspace_size(const kda_prefill_desc *d, size_t 
 
 /* Enqueue the prefill.  Errors: NULL (q/k/v/g/beta/o, or ckpt when ckpt_every > 0,
  * or workspace when one is needed), SHAPE (negative sizes, ckpt_every not a
- * multiple of chunk, n_segments > number of chunks), UNSUPPORTED (d != 128, chunk
+ * multiple of chunk, n_segments > number of chunks, 2^31 or more (sequence, head,
+ * chunk) triples), UNSUPPORTED (d != 128, chunk
  * not 16/64, bad dtype, v_split not 0/1/2), WORKSPACE, ALIAS (o overlapping an
  * input, or S_final overlapping an input other than S0), DEVICE, HIP. */
 KDA_API kda_status kda_prefill_chunked(const kda_prefill_desc *d, hipStream_t stream);
@@ -156,7 +157,8 @@ typedef struct kda_decode_desc {
   float norm_eps;
 } kda_decode_desc;
 
-/* Errors: NULL, SHAPE, UNSUPPORTED, ALIAS, DEVICE, HIP as for the prefill. */
+/* Errors: NULL, SHAPE (negative sizes, N * H of 2^31 or more), UNSUPPORTED, ALIAS,
+ * DEVICE, HIP as for the prefill. */
 KDA_API kda_status kda_decode_step(const kda_decode_desc *d, hipStream_t stream);
 
 /*
@@ -247,7 +249,8 @@ typedef struct kda_backward_desc {
 KDA_API kda_status kda_backward_workspace_size(const kda_backward_desc *d, size_t *bytes);
 
 /* Enqueue the backward pass.  Errors: NULL (an input, dO or a gradient output when
- * B*T*H > 0; workspace), SHAPE (negative sizes), UNSUPPORTED (d != 128, chunk != 64,
+ * B*T*H > 0; workspace), SHAPE (negative sizes, 2^31 or more (sequence, head, chunk)
+ * triples), UNSUPPORTED (d != 128, chunk != 64,
  * bad dtype), WORKSPACE, ALIAS (a gradient output overlapping an input, another
  * output or the workspace), DEVICE, HIP. */
 KDA_API kda_status kda_prefill_backward(const kda_backward_desc *d, hipStream_t stream);

@@ -104,6 +104,9 @@ kda_status validate_sizes(const kda_prefill_desc *d) {
     return KDA_ERR_UNSUPPORTED;
   if (d->n_segments < 0) return KDA_ERR_SHAPE;
   if (d->ckpt_every < 0 || (d->ckpt_every > 0 && d->ckpt_every % d->chunk != 0)) return KDA_ERR_SHAPE;
+  // one prep workgroup per (sequence, head, chunk): the grid is 32-bit
+  const int64_t n_chunks = (static_cast<int64_t>(d->T) + d->chunk - 1) / d->chunk;
+  if (static_cast<int64_t>(d->B) * d->H * n_chunks >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;
   return KDA_OK;
 }
 
@@ -157,6 +160,7 @@ kda_status validate_prefill(const kda_prefill_desc *d, PrefillPlan *p) {
 kda_status validate_decode(const kda_decode_desc *d, int64_t n_state) {
   if (!d) return KDA_ERR_NULL;
   if (d->N < 0 || d->H < 0 || n_state < 0) return KDA_ERR_SHAPE;
+  if (static_cast<int64_t>(d->N) * d->H >= (int64_t(1) << 31)) return KDA_ERR_SHAPE;   // one workgroup per state
   if (d->d_k != 128 || d->d_v != 128) return KDA_ERR_UNSUPPORTED;
   if (!valid_dtype(d->in_dtype) || !valid_dtype(d->out_dtype)) return KDA_ERR_UNSUPPORTED;
   const size_t n = static_cast<size_t>(d->N) * d->H;

@@ -89,6 +89,7 @@ def test_prefill_validation_errors():
     assert _call(_desc(B=-1)) == kda.KDA_ERR_SHAPE
     assert _call(_desc(ckpt_every=100)) == kda.KDA_ERR_SHAPE
     assert _call(_desc(n_segments=3)) == kda.KDA_ERR_SHAPE           # 2 chunks only
+    assert _call(_desc(B=1 << 16, H=1 << 15, T=64)) == kda.KDA_ERR_SHAPE   # 2^31 chunk-heads
     assert _call(_desc(q=None)) == kda.KDA_ERR_NULL
     assert _call(_desc(ckpt_every=64)) == kda.KDA_ERR_NULL            # ckpt missing
     d = _desc()
@@ -138,6 +139,7 @@ def test_decode_validation_errors():
     assert lib.kda_decode_step(None, None) == kda.KDA_ERR_NULL
     assert f(_ddesc(d_v=64)) == kda.KDA_ERR_UNSUPPORTED
     assert f(_ddesc(N=-2)) == kda.KDA_ERR_SHAPE
+    assert f(_ddesc(N=1 << 16, H=1 << 15)) == kda.KDA_ERR_SHAPE       # 2^31 states
     assert f(_ddesc(state=None)) == kda.KDA_ERR_NULL
     d = _ddesc()
     d.o = d.q
