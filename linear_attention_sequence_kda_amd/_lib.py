@@ -161,6 +161,85 @@ def _stream(stream):
     return stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else stream
 
 
+def _expect(name, t, shape, dtypes, device=None, optional=False):
+    """Raise ValueError unless `t` has exactly `shape` and one of `dtypes` (and lives on
+    `device` when given).  Checked before any pointer is taken, so a mis-shaped or
+    mis-typed tensor never reaches a kernel."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype not in dtypes:
+        want = " or ".join(str(d).replace("torch.", "") for d in dtypes)
+        raise ValueError(f"{name} has dtype {str(t.dtype).replace('torch.', '')}, expected {want}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device} (the device of q)")
+
+
+_IN_DTYPES = (torch.float32, torch.bfloat16)
+_F32 = (torch.float32,)
+
+
+def _check_prefill(q, k, v, g, beta, o, S0, S_final, gate, norm_weight, ckpt_every, ckpt,
+                   workspace, need_o=True):
+    """Shapes and dtypes of every prefill tensor against q: [B,T,H,d_k]."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a 4-d tensor [B, T, H, d_k]")
+    _expect("q", q, q.shape, _IN_DTYPES)
+    B, T, H, dk = (int(x) for x in q.shape)
+    dev = q.device
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise ValueError("v must be a 4-d tensor [B, T, H, d_v]")
+    dv = int(v.shape[-1])
+    _expect("k", k, (B, T, H, dk), (q.dtype,), dev)
+    _expect("v", v, (B, T, H, dv), (q.dtype,), dev)
+    _expect("g", g, (B, T, H, dk), _F32, dev)
+    _expect("beta", beta, (B, T, H), _F32, dev)
+    _expect("o", o, (B, T, H, dv), _IN_DTYPES, dev, optional=not need_o)
+    _expect("S0", S0, (B, H, dk, dv), _F32, dev, optional=True)
+    _expect("S_final", S_final, (B, H, dk, dv), _F32, dev, optional=True)
+    _expect("gate", gate, (B, T, H, dv), (q.dtype,), dev, optional=True)
+    _expect("norm_weight", norm_weight, (dv,), _F32, dev, optional=True)
+    every = int(ckpt_every)
+    if every < 0:
+        raise ValueError("ckpt_every must be >= 0")
+    if every > 0:
+        _expect("ckpt", ckpt, (B, T // every, H, dk, dv), _F32, dev,
+                optional=(B * H * (T // every) == 0))
+    elif ckpt is not None:
+        raise ValueError("ckpt given without ckpt_every")
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.device != dev:
+            raise ValueError(f"workspace must be a tensor on {dev}")
+
+
+def _check_decode(q, k, v, g, beta, state, o, gate, norm_weight, pooled=False):
+    """Shapes and dtypes of every decode tensor against q: [N,H,d_k]; the state holds N
+    states per head, or any number (the pool) for the pooled step."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 3:
+        raise ValueError("q must be a 3-d tensor [N, H, d_k]")
+    _expect("q", q, q.shape, _IN_DTYPES)
+    N, H, dk = (int(x) for x in q.shape)
+    dev = q.device
+    if not isinstance(v, torch.Tensor) or v.dim() != 3:
+        raise ValueError("v must be a 3-d tensor [N, H, d_v]")
+    dv = int(v.shape[-1])
+    _expect("k", k, (N, H, dk), (q.dtype,), dev)
+    _expect("v", v, (N, H, dv), (q.dtype,), dev)
+    _expect("g", g, (N, H, dk), _F32, dev)
+    _expect("beta", beta, (N, H), _F32, dev)
+    if not isinstance(state, torch.Tensor) or state.dim() != 4:
+        raise ValueError("state must be a 4-d tensor [N, H, d_k, d_v]")
+    _expect("state", state, (int(state.shape[0]) if pooled else N, H, dk, dv), _F32, dev)
+    _expect("o", o, (N, H, dv), _IN_DTYPES, dev)
+    _expect("gate", gate, (N, H, dv), (q.dtype,), dev, optional=True)
+    _expect("norm_weight", norm_weight, (dv,), _F32, dev, optional=True)
+
+
 def kda_abi_version() -> int:
     return int(load().kda_abi_version())
 
@@ -168,6 +247,8 @@ def kda_abi_version() -> int:
 def _prefill_desc(q, k, v, g, beta, *, o, S0=None, S_final=None, gate=None, norm_weight=None,
                   norm_eps=1e-6, chunk=64, ckpt_every=0, ckpt=None, n_segments=0, v_split=0,
                   workspace=None) -> PrefillDesc:
+    _check_prefill(q, k, v, g, beta, o, S0, S_final, gate, norm_weight, ckpt_every, ckpt,
+                   workspace, need_o=o is not None)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     d = PrefillDesc()
@@ -213,7 +294,8 @@ def kda_prefill_chunked(q, k, v, g, beta, *, o, S0=None, S_final=None, gate=None
     _check("kda_prefill_chunked", load().kda_prefill_chunked(C.byref(d), _stream(stream)))
 
 
-def _decode_desc(q, k, v, g, beta, state, o, gate, norm_weight, norm_eps) -> DecodeDesc:
+def _decode_desc(q, k, v, g, beta, state, o, gate, norm_weight, norm_eps, pooled=False) -> DecodeDesc:
+    _check_decode(q, k, v, g, beta, state, o, gate, norm_weight, pooled)
     N, H, dk = q.shape
     d = DecodeDesc()
     d.N, d.H, d.d_k, d.d_v = N, H, dk, v.shape[-1]
@@ -235,9 +317,8 @@ def kda_decode_step_pooled(q, k, v, g, beta, pool, slots, *, o, gate=None, norm_
                            norm_eps=1e-6, stream=None) -> None:
     """One decode step for [N,H,*] inputs whose states are pool[slots[n]]: `pool`
     [P,H,128,128] float32 is updated in place; `slots` is an int32 device tensor [N]."""
-    if slots is not None and slots.numel() != q.shape[0]:
-        raise ValueError("slots must hold one slot per sequence")
-    d = _decode_desc(q, k, v, g, beta, pool, o, gate, norm_weight, norm_eps)
+    _expect("slots", slots, (int(q.shape[0]),), (torch.int32,), q.device)
+    d = _decode_desc(q, k, v, g, beta, pool, o, gate, norm_weight, norm_eps, pooled=True)
     _check("kda_decode_step_pooled",
            load().kda_decode_step_pooled(C.byref(d), _slots(slots), int(pool.shape[0]),
                                          _stream(stream)))
@@ -255,6 +336,14 @@ def kda_state_copy_indexed(dst, src, *, dst_slots=None, src_slots=None, n=None,
         raise ValueError("dst and src states differ in shape")
     if n is None:
         n = (dst_slots if dst_slots is not None else src_slots if src_slots is not None else dst).shape[0]
+    n = int(n)
+    for name, sl in (("dst_slots", dst_slots), ("src_slots", src_slots)):
+        if sl is None:
+            continue
+        if not isinstance(sl, torch.Tensor) or sl.dim() != 1 or sl.dtype != torch.int32:
+            raise ValueError(f"{name} must be a 1-d int32 tensor")
+        if sl.shape[0] < n:
+            raise ValueError(f"{name} holds {sl.shape[0]} slots, fewer than n = {n}")
     elems = 1
     for x in dst.shape[1:]:
         elems *= int(x)
@@ -272,6 +361,10 @@ def kda_state_checkpoint(state, ckpt, *, stream=None) -> None:
     """ckpt[...] = state[...] (fp32 states of shape [..., d_k, d_v])."""
     if ckpt.shape != state.shape:
         raise ValueError("state and checkpoint shapes differ")
+    if state.dtype != torch.float32 or ckpt.dtype != torch.float32:
+        raise ValueError("states and checkpoints are float32")
+    if state.dim() < 2:
+        raise ValueError("states have shape [..., d_k, d_v]")
     _check("kda_state_checkpoint",
            load().kda_state_checkpoint(_ptr(state), _ptr(ckpt), _n_states(state), state.shape[-2],
                                        state.shape[-1], _stream(stream)))
@@ -281,6 +374,10 @@ def kda_state_rollback(state, ckpt, *, stream=None) -> None:
     """state[...] = ckpt[...] (fp32 states of shape [..., d_k, d_v])."""
     if ckpt.shape != state.shape:
         raise ValueError("state and checkpoint shapes differ")
+    if state.dtype != torch.float32 or ckpt.dtype != torch.float32:
+        raise ValueError("states and checkpoints are float32")
+    if state.dim() < 2:
+        raise ValueError("states have shape [..., d_k, d_v]")
     _check("kda_state_rollback",
            load().kda_state_rollback(_ptr(state), _ptr(ckpt), _n_states(state), state.shape[-2],
                                      state.shape[-1], _stream(stream)))
@@ -318,7 +415,14 @@ def kda_prefill_backward(q, k, v, g, beta, dO, *, dq, dk, dv, dg, dbeta, S0=None
     dS_final, dS0: [B,H,128,128] float32 or None.  dq, dk, dv, dg: [B,T,H,128] float32;
     dbeta: [B,T,H] float32.  Without a workspace, one is allocated from torch's caching
     allocator."""
+    if not isinstance(q, torch.Tensor) or q.dim() != 4 or not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise ValueError("q and v must be 4-d tensors [B, T, H, d]")
+    _expect("q", q, q.shape, _IN_DTYPES)
     B, T, H, dk_ = q.shape
+    _expect("k", k, q.shape, (q.dtype,), q.device)
+    _expect("v", v, (B, T, H, v.shape[-1]), (q.dtype,), q.device)
+    _expect("g", g, q.shape, _F32, q.device)
+    _expect("beta", beta, (B, T, H), _F32, q.device)
     for name, t, shape in (("dO", dO, (B, T, H, v.shape[-1])), ("dq", dq, q.shape), ("dk", dk, q.shape),
                            ("dv", dv, v.shape), ("dg", dg, g.shape), ("dbeta", dbeta, beta.shape),
                            ("S0", S0, (B, H, dk_, v.shape[-1])), ("dS_final", dS_final, (B, H, dk_, v.shape[-1])),
