@@ -4,12 +4,19 @@
 
 Compiles every source under csrc/ into _build/ and links the shared library next to
 this file.  Always rebuilds (the sources are small); objects are compiled in parallel.
+
+Every compile also asks the compiler for each kernel's resource usage, and the build
+fails if any kernel needs scratch memory (register spills).  Several kernels wait for
+their own global->LDS copies and loads with exact vector-memory counts, and order LDS
+with barriers that do not wait for vector memory: both assume that the compiler adds no
+memory operation of its own, which a spill to scratch would.
 """
 from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -34,9 +41,41 @@ COMMON = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+RESOURCE_FLAG = "-Rpass-analysis=kernel-resource-usage"
+
+
+def kernel_resources(remarks: str) -> dict:
+    """{kernel symbol: {"vgpr": n, "agpr": n, "scratch": bytes per lane, "lds": bytes}} parsed
+    from the compiler's kernel-resource-usage remarks."""
+    out, cur = {}, None
+    keys = {"VGPRs": "vgpr", "AGPRs": "agpr", "ScratchSize [bytes/lane]": "scratch",
+            "LDS Size [bytes/block]": "lds"}
+    for line in remarks.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+(VGPRs|AGPRs|ScratchSize \[bytes/lane\]|LDS Size \[bytes/block\]): (\d+)", line)
+        if m and cur is not None:
+            cur[keys[m.group(1)]] = int(m.group(2))
+    return out
+
+
+def check_no_scratch(src: str, remarks: str) -> dict:
+    """Raise if a kernel of `src` spills to scratch; return its resource table."""
+    res = kernel_resources(remarks)
+    if src.endswith(".hip") and not res:
+        raise RuntimeError(f"{src}: the compiler reported no kernel resource usage")
+    spill = {k: v["scratch"] for k, v in res.items() if v.get("scratch", 0) > 0}
+    if spill:
+        raise RuntimeError(f"{src}: kernels use scratch memory (register spills), which breaks "
+                           f"their exact memory wait counts: {spill}")
+    return res
+
+
+def _compile(src: str, verbose: bool, out_dir: str = BUILD) -> str:
+    obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *COMMON, RESOURCE_FLAG, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     if verbose:
@@ -44,8 +83,11 @@ def _compile(src: str, verbose: bool) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")
-    if verbose and r.stderr.strip():
-        print(r.stderr, file=sys.stderr)
+    check_no_scratch(src, r.stderr)
+    if verbose:
+        warn = [l for l in r.stderr.splitlines() if RESOURCE_FLAG not in l]
+        if warn:
+            print("\n".join(warn), file=sys.stderr)
     return obj
 
 

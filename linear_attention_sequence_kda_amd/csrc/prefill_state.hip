@@ -438,7 +438,10 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
     // ahead of the product that consumes them, in the order the products below take
     // them (SeqFrags), so that LDS latency overlaps the matrix cores.
     using SF = SeqFrags<C, F32, MODE == MODE_OUTPUT>;
-    constexpr int PF = SF::n < 4 ? SF::n : 4;
+    // (fp32 fragments are twice as wide: a two-deep ring keeps the gated fp32 pass
+    // within its registers, with no scratch)
+    constexpr int PF_MAX = F32 && GATE ? 2 : 4;
+    constexpr int PF = SF::n < PF_MAX ? SF::n : PF_MAX;
     auto fetch = [&](int i) __attribute__((always_inline)) {
       return Op<F32>::load(reinterpret_cast<const T *>(rc + SF::seq.off[i] + lane * 8 * sizeof(T)));
     };
