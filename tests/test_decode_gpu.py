@@ -114,6 +114,30 @@ def test_decode_workload_shape_sampled():
     assert torch.isfinite(S_dev).all()
 
 
+def test_decode_workload_all_states():
+    """The whole decode workload (256 sequences x 16 heads, state N(0, 0.05)) for its first
+    24 steps: every output of every step and every final state against the oracle."""
+    N, H, steps, seed = 256, 16, 24, 0
+    _say("decode workload, all states: generating inputs")
+    S_np = make_decode_state(N, H, 128, seed=seed)
+    X = make_decode_steps(N, H, 128, seed=seed, steps=steps)
+    Xd = {k: up(v) for k, v in X.items()}
+    S_dev = up(S_np)
+    o_all = torch.empty((steps, N, H, 128), dtype=torch.float32, device=dev())
+    for s in range(steps):
+        kda.kda_decode_step(Xd["q"][s], Xd["k"][s], Xd["v"][s], Xd["g"][s], Xd["beta"][s], S_dev,
+                            o=o_all[s])
+    torch.cuda.synchronize()
+    _say("decode workload, all states: oracle")
+    S_ref = S_np.astype(np.float64)
+    o_ref = np.stack([native.decode_step(S_ref, X["q"][s], X["k"][s], X["v"][s], X["g"][s],
+                                         X["beta"][s], bf16=True) for s in range(steps)])
+    e, eS = err_o(down(o_all), o_ref), err_S(down(S_dev), S_ref)
+    _say(f"decode workload, all states: err_o={e:.3e} err_S={eS:.3e}")
+    assert e <= TOL_DECODE
+    assert eS <= 1e-5
+
+
 def test_speculative_rollback_bit_exact():
     """60 steps, checkpoint, 4 speculative steps, rollback: the restored state equals the
     checkpoint bit for bit and the oracle state after step 60; 4 replacement steps with

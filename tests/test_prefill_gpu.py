@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import linear_attention_sequence_kda_amd as kda
-from kda_inputs import BF16, F32, make_prefill, to_f64
+from kda_inputs import BF16, F32, f32_to_bf16, make_prefill, to_f64
 from oracle import native, norm_gate
 from gpu_util import up, down, err_o, err_S, bf16_out_tol, dev
 
@@ -246,3 +246,31 @@ def test_s_final_may_alias_s0():
     torch.cuda.synchronize()
     _, S_ref, _ = run_ref(c)
     assert err_S(down(S), S_ref) <= TOL_S_BF16
+
+
+# ---------------------------------------------------------------------------
+# large value magnitudes: v and the state far from the unit scale the workloads draw
+# ---------------------------------------------------------------------------
+def _scaled_values(c, lo_exp, hi_exp, s0_std, seed):
+    """Scale every (token, head) row of v so that its largest magnitude is 10^u,
+    u ~ U(lo_exp, hi_exp), and draw S0 with standard deviation s0_std: large but
+    bf16-representable inputs."""
+    rng = np.random.default_rng([seed, 991])
+    v = to_f64(c.v, BF16)
+    f = 10.0 ** rng.uniform(lo_exp, hi_exp, size=v.shape[:-1] + (1,)) / np.max(np.abs(v), -1, keepdims=True)
+    c.v = f32_to_bf16((v * f).astype(np.float32))
+    c.S0 = (rng.standard_normal(c.S0.shape) * s0_std).astype(np.float32)
+    return c
+
+
+@pytest.mark.parametrize("plan", [dict(chunk=64), dict(chunk=64, n_segments=3, ckpt_every=128),
+                                  dict(chunk=16, gate=True), dict(chunk=64, v_split=2, gate=True)],
+                         ids=["c64", "c64-seg3-ckpt", "c16-gate", "c64-vsplit2-gate"])
+def test_large_magnitudes(plan):
+    """Rows of v with largest magnitudes from 1e3 to 3e4 and S0 entries ~1e3: the fp16
+    operands of the state products (v, the state copy, U) stay inside their range and
+    the parity bound holds."""
+    c = make_prefill(2, 650, 2, 128, seed=97, in_dtype=BF16, s0_std=1.0, gate=plan.get("gate", False))
+    c = _scaled_values(c, 3.0, np.log10(3e4), 1e3, seed=97)
+    assert 2e4 < np.max(np.abs(to_f64(c.v, BF16))) <= 3.01e4
+    check(c, f"large magnitudes {plan}", **plan)

@@ -4,9 +4,10 @@ times (automatic plan unless a test names one), against the fp64 CPU oracle.
   prefill_8k    B=4, H=16, T=8192, chunk 64, norm + gate, S0 ~ N(0, 0.01): all heads
   prefill_131k  B=1, H=16, T=131072, floor-pinned and slow channels, 512-token
                 checkpoints: all heads, every checkpoint
-  prefill_1m    B=1, H=8, T=2^20 over 256 segments: two sampled heads (the oracle
-                follows them token by token), then 64 decode steps on all heads with
-                a 4-step speculative rollback
+  prefill_1m    B=1, H=8, T=2^20 over 256 segments: all eight heads (the oracle runs
+                two heads at a time to bound host memory; err_o is taken over the whole
+                tensor), then 64 decode steps on all heads with a 4-step speculative
+                rollback
 Tolerances as in test_prefill_gpu.py (bf16 inputs): err_o <= 2e-2, err_S <= 1e-2;
 decode err_o <= 1e-4.
 """
@@ -67,7 +68,7 @@ def test_prefill_131k_with_checkpoints():
                                           ckpt_every=every)
     og = down(o)
     eo, es = err_o(og, o_ref), err_S(down(S), S_ref)
-    ck_err = max(err_S(down(ck[:, m]), ck_ref[:, m]) for m in range(0, c.T // every, 7))
+    ck_err = max(err_S(down(ck[:, m]), ck_ref[:, m]) for m in range(c.T // every))
     _say(f"prefill_131k: err_o={eo:.3e} err_S={es:.3e} max ckpt err_S={ck_err:.3e}")
     assert np.isfinite(og).all()
     assert eo <= TOL_O and es <= TOL_S and ck_err <= TOL_S
@@ -83,17 +84,24 @@ def test_prefill_1m_segments_then_decode_with_rollback():
     kda.kda_prefill_chunked(up(c.q), up(c.k), up(c.v), up(c.g), up(c.beta), o=o, S_final=S,
                             chunk=64, n_segments=256)
     torch.cuda.synchronize()
-    heads = [1, 6]
-    _say(f"prefill_1m: oracle on heads {heads}")
-    sl = lambda x: np.ascontiguousarray(x[:, :, heads])  # noqa: E731
-    o_ref, S_ref, _ = native.prefill(sl(c.q), sl(c.k), sl(c.v), sl(c.g), sl(c.beta), None,
-                                     bf16=True)
-    og = down(o[:, :, heads])
-    eo, es = err_o(og, o_ref), err_S(down(S[:, heads]), S_ref)
+    # whole tensor, two heads at a time: err_o = max |o - o_ref| / rms(o_ref) over all of it
+    max_abs, sumsq, count, S_ref = 0.0, 0.0, 0, np.empty((c.B, c.H, 128, 128))
+    for h0 in range(0, c.H, 2):
+        heads = [h0, h0 + 1]
+        _say(f"prefill_1m: oracle on heads {heads}")
+        sl = lambda x: np.ascontiguousarray(x[:, :, heads])  # noqa: E731
+        o_ref, S_ref[:, heads], _ = native.prefill(sl(c.q), sl(c.k), sl(c.v), sl(c.g), sl(c.beta),
+                                                   None, bf16=True)
+        og = down(o[:, :, heads])
+        assert np.isfinite(og).all()
+        max_abs = max(max_abs, float(np.max(np.abs(og - o_ref))))
+        sumsq += float(np.sum(o_ref * o_ref))
+        count += o_ref.size
+        del og, o_ref
+    eo, es = max_abs / np.sqrt(sumsq / count), err_S(down(S), S_ref)
     _say(f"prefill_1m: err_o={eo:.3e} err_S={es:.3e}")
-    assert np.isfinite(og).all()
     assert eo <= TOL_O and es <= TOL_S
-    del o, og, o_ref
+    del o
 
     # decode tail: 60 steps, checkpoint, 4 speculative steps, rollback, 4 fresh steps.
     # GPU states continue from the GPU prefill; the oracle states from the GPU prefill
