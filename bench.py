@@ -1,18 +1,27 @@
 """Benchmark of the KDA hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-backward]
+                    [--no-long] [--no-decode]
 
 Headline (`value`): chunkwise prefill tokens/s on the prefill workload B=4, H=16,
 T=8192, d=128, chunk 64, bf16 q/k/v/gate, fp32 g/beta/state, S0 ~ N(0, 0.01), with the
 fused per-head RMSNorm and sigmoid gate, fp32 output.  One step = one prefill call over
-the whole batch with inputs resident in HBM.  The same run also times the decode
-workload (256 sequences x 16 heads, fp32 states, one kernel per step) and reports its
-sequence-steps/s, decode over a pool of state slots, and the backward pass of the same
-prefill (gradients of the raw outputs, fp32 MFMA) against the fp32 matrix peak.
+the whole batch with inputs resident in HBM.  The same run also times:
+  - decode, 256 sequences x 16 heads (fp32 states, one kernel per step), stepped over
+    four such state sets in turn so that every step's 256 MiB of state comes from DRAM,
+    not from the 256 MB last-level cache; and the same step on one state set (in cache);
+  - decode over a pool of state slots, with write-back of states to pinned host memory;
+  - the 131k-token prefill (B=1, H=16, 512-token checkpoints);
+  - the 1M-token prefill over 256 segments (B=1, H=8), its 64-step decode tail and the
+    rollback of 8 states;
+  - the backward pass of the 8k prefill (gradients of the raw outputs, fp32 MFMA).
 
-Prints one JSON line with a `roofline` object for the prefill kernel (algorithmic bytes
-over measured duration against 8 TB/s) and a `cpu_baseline` object (the fp64 C oracle
-on the host cores over the same prefill workload).
+Prints one JSON line.  Every leg carries a `roofline` object: algorithmic bytes (each
+input read once, each output written once, in the byte convention of the workload
+table: bf16 activations and outputs, fp32 g, beta and states) over the event-timed
+duration on the launch stream, against 8 TB/s; the backward against the fp32 matrix
+peak.  `cpu_baseline` is the fp64 C oracle on the host cores over the 8k prefill,
+`decode_cpu_baseline` the same oracle stepping the 256 x 16 decode workload.
 """
 from __future__ import annotations
 
@@ -35,11 +44,22 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X dense FP32 MFMA, TFLOP/s
 D = 128
 
 
-def prefill_alg_bytes(B, T, H, out_bytes=4):
-    """Bytes the prefill must move: every input read once, every output written once."""
-    per_tok_head = 3 * D * 2 + D * 4 + 4 + D * 2 + D * out_bytes   # q,k,v bf16; g; beta; gate; o
-    states = 2 * B * H * D * D * 4                                   # S0 in, S_final out
-    return B * T * H * per_tok_head + states
+def prefill_alg_bytes(B, T, H, out_bytes=4, gate=True, ckpt_every=0, s0=True, s_final=True):
+    """Bytes the prefill must move: every input read once, every output written once.
+    Per token-head: q, k, v bf16 (768 B), g fp32 (512), beta (4), the gate bf16 (256) and
+    o (out_bytes per element); checkpoints add one fp32 state per ckpt_every tokens per
+    head (128 B per token-head at 512); S0 and S_final one state per (sequence, head)."""
+    per_tok_head = 3 * D * 2 + D * 4 + 4 + (D * 2 if gate else 0) + D * out_bytes
+    total = B * T * H * per_tok_head
+    if ckpt_every:
+        total += B * (T // ckpt_every) * H * D * D * 4
+    total += (int(s0) + int(s_final)) * B * H * D * D * 4
+    return total
+
+
+def table_prefill_bytes(B, T, H, **kw):
+    """The workload table's convention: outputs counted as bf16 (2 B per element)."""
+    return prefill_alg_bytes(B, T, H, out_bytes=2, **kw)
 
 
 def prefill_alg_flops(B, T, H, chunk=64):
@@ -95,15 +115,18 @@ def _traffic_from_profiles(kernel_hash):
     return None if v is None else int(v)
 
 
+def _cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(c, gate):
     """Time the fp64 C oracle (plus the numpy norm/gate) on the host cores."""
     from oracle import native, norm_gate
     from kda_inputs import to_f64
-    try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count() or 1
-    threads = max(1, min(cores, 64))
+    threads = max(1, min(_cores(), 64))
     # whole passes over the workload until about 10 s of wall time (at most 20 passes)
     passes, dt = 0, 0.0
     while passes < 20 and (passes == 0 or dt < 10.0):
@@ -117,6 +140,38 @@ def cpu_baseline(c, gate):
                        f"H={c.H}), fp64 C recurrence + numpy norm/gate, {dt:.1f} s")
 
 
+def decode_cpu_baseline(S_np, X):
+    """Time the fp64 C oracle stepping the decode workload (all states, the same step
+    inputs the GPU leg uses) on the host cores, for about 5 s."""
+    from oracle import native
+    threads = max(1, min(_cores(), 64))
+    N, H = S_np.shape[:2]
+    S = S_np.astype(np.float64)
+    nx = X["q"].shape[0]
+    steps, dt = 0, 0.0
+    while steps < 200 and (steps < 2 or dt < 5.0):
+        j = steps % nx
+        t0 = time.perf_counter()
+        native.decode_step(S, X["q"][j], X["k"][j], X["v"][j], X["g"][j], X["beta"][j], bf16=True,
+                           nthreads=threads)
+        dt += time.perf_counter() - t0
+        steps += 1
+    return dict(value=N * steps / dt, unit="seq-steps/s", cores=threads, kind="oracle",
+                sample=f"{steps} steps of all {N} sequences x {H} heads (fp64 C recurrence), "
+                       f"{dt:.1f} s")
+
+
+def _roofline(bytes_, ms, **extra):
+    gbs = bytes_ / (ms * 1e-3) / 1e9
+    return dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs / HBM_PEAK_GBS, 4), alg_bytes_per_launch=int(bytes_),
+                kernel_ms_mean=round(ms, 4), **extra)
+
+
+def _say(*x):
+    print(*x, file=sys.stderr, flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +181,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-long", action="store_true", help="skip the 131k and 1M prefill legs")
     ap.add_argument("--v-split", type=int, default=0)
     ap.add_argument("--n-segments", type=int, default=0)
     a = ap.parse_args()
@@ -140,6 +196,7 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
 
     def up(x):
         x = np.ascontiguousarray(x)
@@ -147,8 +204,23 @@ def main():
             else torch.from_numpy(x)
         return t.to(dev)
 
+    def timed(fn, n, warmup):
+        """Mean duration in ms of n calls of fn() back to back, between two events on the
+        launch stream, after `warmup` calls."""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
     # ---------------- prefill workload ----------------
     B, T, H = 4, 8192, 16
+    _say("bench: 8k prefill")
     c = make_workload("prefill_8k", seed=0)
     q, k, v, g, beta, gate, S0 = (up(x) for x in (c.q, c.k, c.v, c.g, c.beta, c.gate, c.S0))
     o = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
@@ -157,13 +229,13 @@ def main():
               v_split=a.v_split, n_segments=a.n_segments)
     ws_bytes = kda.kda_prefill_workspace_size(q, k, v, g, beta, **kw)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
 
     def step():
         kda.kda_prefill_chunked(q, k, v, g, beta, workspace=ws, stream=stream, **kw)
 
     # warm-up calls (the first tens of calls on a fresh GPU run slower while its clocks
-    # ramp up), then K calls back to back between two events on the launch stream
+    # ramp up), then K calls back to back between two events on the launch stream,
+    # bracketed by synchronisations for the wall clock
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -179,10 +251,9 @@ def main():
     ms_step = wall * 1e3 / a.steps
     tokens = B * T
     value = tokens / (ms_step * 1e-3)
-    alg_b = prefill_alg_bytes(B, T, H)
+    alg_b = table_prefill_bytes(B, T, H, gate=True)
     alg_f = prefill_alg_flops(B, T, H)
     kernel_ms = ms_mean
-    achieved = alg_b / (kernel_ms * 1e-3) / 1e9
     khash = _src_hash("tiles.h", "prefill_prep.hip", "prefill_state.hip")
     traffic = _traffic_from_profiles(khash)
 
@@ -197,7 +268,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16-in/fp16-mfma/fp32-acc",
+        "arithmetic": "bf16 q/k/v/gate; BF16 MFMA on the 16-token diagonal tiles (hi/lo split "
+                      "for P), FP16 MFMA for every other product, fp32 accumulation, fp32 state "
+                      "and outputs",
         "data": "synthetic",
         "config": {
             "workload": "prefill B=4 H=16 T=8192 d=128 chunk=64; bf16 q/k/v/gate, fp32 g/beta/"
@@ -205,67 +279,83 @@ def main():
             "global_batch": B, "seq_len": T, "heads": H, "head_dim": D, "chunk": 64,
             "parallelism": "single GPU",
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": traffic,
-            "kernel": "one prefill call per step: chunk_prep_kernel, chunk_state_kernel (state "
-                      "maps), segment_scan, chunk_state_kernel (outputs); their durations sum to "
-                      "the call",
-            "alg_bytes_per_launch": alg_b,
-            "kernel_ms_mean": round(kernel_ms, 4),
-        },
+        "roofline": _roofline(
+            alg_b, kernel_ms, traffic=traffic,
+            kernel="one prefill call per step: chunk_prep_kernel, chunk_state_kernel (state "
+                   "maps), segment_scan, chunk_state_kernel (outputs); their durations sum to "
+                   "the call",
+            bytes_convention="1796 B per token-head (q/k/v/gate bf16, g fp32, beta, o counted "
+                             "as bf16) + S0 and S_final",
+            frac_fp32_out=round(prefill_alg_bytes(B, T, H) / (kernel_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)),
         "prefill_mfma": {
             "alg_flops_per_launch": alg_f,
             "achieved_tflops": round(alg_f / (kernel_ms * 1e-3) / 1e12, 2),
             "peak_tflops": BF16_PEAK_TFLOPS,
             "frac": round(alg_f / (kernel_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         },
+        "workspace_bytes": int(ws_bytes),
     }
 
     # ---------------- decode workload ----------------
     if not a.no_decode:
         N, Hd, steps = 256, 16, a.decode_steps
-        S_np = make_decode_state(N, Hd, D, seed=0)
-        Xd = make_decode_steps(N, Hd, D, seed=0, steps=min(steps, 64))
+        _say("bench: decode")
+        Xd = make_decode_steps(N, Hd, D, seed=0, steps=64)
         X = {kk: up(vv) for kk, vv in Xd.items()}
-        St = up(S_np)
         od = torch.empty((N, Hd, D), dtype=torch.float32, device=dev)
         nx = X["q"].shape[0]
+        db = decode_alg_bytes(N, Hd)
+        # four independent state sets of the workload (4 x 256 MiB), stepped in turn: each
+        # step's states were last touched 768 MiB of traffic ago, so they come from DRAM
+        sets = [up(make_decode_state(N, Hd, D, seed=i)) for i in range(4)]
+        S_np0 = make_decode_state(N, Hd, D, seed=0)
+        ctr = [0]
 
-        def dstep(s):
+        def dstep_sets():
+            s = ctr[0]
+            ctr[0] += 1
+            j = s % nx
+            kda.kda_decode_step(X["q"][j], X["k"][j], X["v"][j], X["g"][j], X["beta"][j],
+                                sets[s % 4], o=od, stream=stream)
+
+        us_dram = timed(dstep_sets, steps, 12) * 1e3
+        St = sets[0]
+        ctr[0] = 0
+
+        def dstep_one():
+            s = ctr[0]
+            ctr[0] += 1
             j = s % nx
             kda.kda_decode_step(X["q"][j], X["k"][j], X["v"][j], X["g"][j], X["beta"][j], St,
                                 o=od, stream=stream)
 
-        for s in range(10):
-            dstep(s)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for s in range(steps):
-            dstep(s)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
-        db = decode_alg_bytes(N, Hd)
+        us_cache = timed(dstep_one, steps, 10) * 1e3
         out["decode"] = {
             "workload": "decode 256 sequences x H=16, fp32 128x128 states, bf16 q/k/v, "
-                        f"{steps} single-token steps (inputs cycle over {nx} seeded draws)",
-            "seq_steps_per_s": round(N / (us * 1e-6), 1),
-            "us_per_step": round(us, 2),
-            "roofline": {"bound": "hbm", "achieved": round(db / (us * 1e-6) / 1e9, 1),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(db / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                         "alg_bytes_per_launch": db},
+                        f"{steps} single-token steps (inputs cycle over {nx} seeded draws), over "
+                        "four state sets (1 GiB) in turn: every step reads its 256 MiB of state "
+                        "from DRAM",
+            "seq_steps_per_s": round(N / (us_dram * 1e-6), 1),
+            "us_per_step": round(us_dram, 2),
+            "roofline": _roofline(db, us_dram * 1e-3, kernel="decode_kernel"),
         }
+        out["decode_in_cache"] = {
+            "workload": "the same step on one state set (256 MiB, near the 256 MB last-level "
+                        "cache size): partly served from that cache",
+            "seq_steps_per_s": round(N / (us_cache * 1e-6), 1),
+            "us_per_step": round(us_cache, 2),
+            "roofline": _roofline(db, us_cache * 1e-3, kernel="decode_kernel"),
+        }
+        del sets, St
+        if not a.no_cpu_baseline:
+            _say("bench: decode oracle baseline")
+            out["decode_cpu_baseline"] = decode_cpu_baseline(S_np0, Xd)
+        del S_np0, Xd
 
     # ---------------- serving: decode over a state pool, write-back to host ----------------
     if not a.no_decode:
         P, N, Hs, steps = 1024, 256, 16, 200
+        _say("bench: pooled decode")
         pool = torch.empty((P, Hs, D, D), dtype=torch.float32, device=dev)
         for i in range(0, P, N):                                   # seeded states, 256 at a time
             pool[i:i + N] = up(make_decode_state(N, Hs, D, seed=1 + i // N))
@@ -273,42 +363,25 @@ def main():
         Xp = make_decode_steps(N, Hs, D, seed=1, steps=16)
         XP = {kk: up(vv) for kk, vv in Xp.items()}
         op = torch.empty((N, Hs, D), dtype=torch.float32, device=dev)
+        ctr = [0]
 
-        def pstep(s):
-            j = s % 16
+        def pstep():
+            j = ctr[0] % 16
+            ctr[0] += 1
             kda.kda_decode_step_pooled(XP["q"][j], XP["k"][j], XP["v"][j], XP["g"][j], XP["beta"][j],
                                        pool, slots, o=op, stream=stream)
 
-        for s in range(5):
-            pstep(s)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for s in range(steps):
-            pstep(s)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
+        us = timed(pstep, steps, 5) * 1e3
         db = decode_alg_bytes(N, Hs) + N * 4
         # write-back of the active sequences' states to pinned host memory
         host = torch.empty((N, Hs, D, D), dtype=torch.float32, pin_memory=True)
-        kda.kda_state_copy_indexed(host, pool, src_slots=slots, stream=stream)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(3):
-            kda.kda_state_copy_indexed(host, pool, src_slots=slots, stream=stream)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        wb_ms = e0.elapsed_time(e1) / 3
+        wb_ms = timed(lambda: kda.kda_state_copy_indexed(host, pool, src_slots=slots, stream=stream), 3, 1)
         out["decode_pooled"] = {
             "workload": f"decode over a pool of {P} sequences x H={Hs} (fp32 states, 1 GiB), "
                         f"{N} active sequences at seeded slots, {steps} steps",
             "seq_steps_per_s": round(N / (us * 1e-6), 1),
             "us_per_step": round(us, 2),
-            "roofline": {"bound": "hbm", "achieved": round(db / (us * 1e-6) / 1e9, 1),
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(db / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                         "alg_bytes_per_launch": db},
+            "roofline": _roofline(db, us * 1e-3, kernel="decode_kernel (pooled)"),
             "write_back_to_pinned_host": {"bytes": N * Hs * D * D * 4, "ms": round(wb_ms, 3),
                                           "GB_per_s": round(N * Hs * D * D * 4 / (wb_ms * 1e-3) / 1e9, 1)},
         }
@@ -317,6 +390,7 @@ def main():
     # ---------------- backward of the prefill (training) ----------------
     if not a.no_backward:
         from kda_inputs import make_output_grads
+        _say("bench: backward")
         dO_np, dS_np = make_output_grads(B, T, H, D, seed=0)
         dO, dSf = up(dO_np), up(dS_np)
         del dO_np
@@ -330,17 +404,7 @@ def main():
             kda.kda_prefill_backward(q, k, v, g, beta, dO, S0=S0, dS_final=dSf, workspace=bws,
                                      stream=stream, **grads)
 
-        for _ in range(5):
-            bstep()
-        torch.cuda.synchronize()
-        nb = 10
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(nb):
-            bstep()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        bms = e0.elapsed_time(e1) / nb
+        bms = timed(bstep, 10, 5)
         bf = backward_alg_flops(B, T, H)
         out["backward"] = {
             "workload": "gradients of the raw-output prefill above (same q/k/v/g/beta/S0; "
@@ -355,15 +419,91 @@ def main():
         }
         del grads, bws, dO, dSf
 
-    # one copy kernel of known size (state checkpoint, 64 MiB each way) after the timed regions:
+    # one copy kernel of known size (state checkpoint, 64 MiB each way) after the 8k legs:
     # counter runs use it to calibrate FETCH_SIZE / WRITE_SIZE against known bytes
     cal_src = torch.zeros((1024, D, D), dtype=torch.float32, device=dev)
     cal_dst = torch.empty_like(cal_src)
     kda.kda_state_checkpoint(cal_src, cal_dst, stream=stream)
     torch.cuda.synchronize()
+    del cal_src, cal_dst
 
     if not a.no_cpu_baseline:
+        _say("bench: prefill oracle baseline")
         out["cpu_baseline"] = cpu_baseline(c, gate=True)
+    del q, k, v, g, beta, gate, S0, o, Sf, ws, c
+
+    # ---------------- long sequences: 131k with checkpoints, 1M over 256 segments ----------------
+    if not a.no_long:
+        _say("bench: 131k prefill")
+        c3 = make_workload("prefill_131k", seed=0)
+        T3, H3, every = c3.T, c3.H, 512
+        t3 = [up(x) for x in (c3.q, c3.k, c3.v, c3.g, c3.beta)]
+        del c3
+        o3 = torch.empty((1, T3, H3, D), dtype=torch.float32, device=dev)
+        S3 = torch.empty((1, H3, D, D), dtype=torch.float32, device=dev)
+        ck3 = torch.empty((1, T3 // every, H3, D, D), dtype=torch.float32, device=dev)
+        kw3 = dict(o=o3, S_final=S3, chunk=64, ckpt_every=every, ckpt=ck3)
+        ws3 = torch.empty(max(1, kda.kda_prefill_workspace_size(*t3, **kw3)), dtype=torch.uint8, device=dev)
+        ms3 = timed(lambda: kda.kda_prefill_chunked(*t3, workspace=ws3, stream=stream, **kw3), 10, 3)
+        b3 = table_prefill_bytes(1, T3, H3, gate=False, ckpt_every=every, s0=False)
+        out["prefill_131k"] = {
+            "workload": "prefill B=1 H=16 T=131072 chunk 64, 10% of channels at the -5 floor and "
+                        "10% slow-decaying, checkpoints every 512 tokens (256 MiB), fp32 out",
+            "ms_per_call": round(ms3, 3),
+            "tokens_per_s": round(T3 / (ms3 * 1e-3), 1),
+            "roofline": _roofline(b3, ms3, bytes_convention="1540 B per token-head (o counted as "
+                                  "bf16) + 128 B of checkpoints + S_final"),
+            "mfma_frac": round(prefill_alg_flops(1, T3, H3) / (ms3 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "workspace_bytes": int(ws3.numel()),
+        }
+        del t3, o3, S3, ck3, ws3
+
+        _say("bench: 1M prefill")
+        c4 = make_workload("prefill_1m", seed=0)
+        T4, H4 = c4.T, c4.H
+        t4 = [up(x) for x in (c4.q, c4.k, c4.v, c4.g, c4.beta)]
+        del c4
+        o4 = torch.empty((1, T4, H4, D), dtype=torch.float32, device=dev)
+        S4 = torch.empty((1, H4, D, D), dtype=torch.float32, device=dev)
+        kw4 = dict(o=o4, S_final=S4, chunk=64, n_segments=256)
+        ws4 = torch.empty(max(1, kda.kda_prefill_workspace_size(*t4, **kw4)), dtype=torch.uint8, device=dev)
+        ms4 = timed(lambda: kda.kda_prefill_chunked(*t4, workspace=ws4, stream=stream, **kw4), 3, 1)
+        b4 = table_prefill_bytes(1, T4, H4, gate=False, s0=False)
+        leg = {
+            "workload": "prefill B=1 H=8 T=1048576 chunk 64 over 256 segments combined by the "
+                        "associative scan of their state maps, fp32 out",
+            "ms_per_call": round(ms4, 3),
+            "tokens_per_s": round(T4 / (ms4 * 1e-3), 1),
+            "roofline": _roofline(b4, ms4, bytes_convention="1540 B per token-head (o counted as "
+                                  "bf16) + S_final"),
+            "mfma_frac": round(prefill_alg_flops(1, T4, H4) / (ms4 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "workspace_bytes": int(ws4.numel()),
+        }
+        del t4, o4, ws4
+        # decode tail: 64 single-token steps of the one sequence from the prefill's final
+        # state, then the rollback of its 8 states from a checkpoint
+        Xt = {kk: up(vv) for kk, vv in make_decode_steps(1, H4, D, seed=7, steps=64).items()}
+        st = S4.clone()
+        ot = torch.empty((1, H4, D), dtype=torch.float32, device=dev)
+        ctr = [0]
+
+        def tstep():
+            j = ctr[0] % 64
+            ctr[0] += 1
+            kda.kda_decode_step(Xt["q"][j], Xt["k"][j], Xt["v"][j], Xt["g"][j], Xt["beta"][j], st,
+                                o=ot, stream=stream)
+
+        us_tail = timed(tstep, 64, 4) * 1e3
+        ckt = torch.empty_like(st)
+        kda.kda_state_checkpoint(st, ckt, stream=stream)
+        us_rb = timed(lambda: kda.kda_state_rollback(st, ckt, stream=stream), 50, 5) * 1e3
+        leg["decode_tail"] = {"us_per_step": round(us_tail, 2), "steps": 64,
+                              "note": "one sequence x 8 heads: 8 workgroups, bound by launch and "
+                                      "memory latency, not bandwidth"}
+        leg["rollback"] = {"us": round(us_rb, 2), "states": H4, "bytes": H4 * D * D * 4}
+        out["prefill_1m"] = leg
+        del S4, st, ckt, Xt
+
     print(json.dumps(out), flush=True)
 
 

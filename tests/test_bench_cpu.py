@@ -23,6 +23,18 @@ def test_prefill_alg_bytes_per_token_head():
     assert bench.prefill_alg_bytes(1, 1, 1, out_bytes=2) - 2 * 128 * 128 * 4 == 2052 - 256
 
 
+def test_table_bytes_match_the_workload_table():
+    """The roofline's byte convention: bf16 activations and outputs, fp32 g, beta and states.
+    8k prefill 1796 B per token-head + S0/S_T = 0.950 GB; 131k 1540 B + 128 B of 512-token
+    checkpoints = 3.50 GB; 1M 1540 B = 12.9 GB."""
+    c1 = bench.table_prefill_bytes(4, 8192, 16, gate=True)
+    assert c1 == 4 * 8192 * 16 * 1796 + 2 * 4 * 16 * 65536 and round(c1 / 1e9, 3) == 0.950
+    c3 = bench.table_prefill_bytes(1, 131072, 16, gate=False, ckpt_every=512, s0=False)
+    assert c3 == 131072 * 16 * (1540 + 128) + 16 * 65536 and round(c3 / 1e9, 2) == 3.50
+    c4 = bench.table_prefill_bytes(1, 1 << 20, 8, gate=False, s0=False)
+    assert c4 == (1 << 20) * 8 * 1540 + 8 * 65536 and round(c4 / 1e10, 2) == 1.29
+
+
 def test_decode_alg_bytes_per_state():
     # state read and written (2 x 64 KiB), q/k/v bf16, g fp32, beta, o fp32
     assert bench.decode_alg_bytes(1, 1) == 2 * 65536 + 3 * 256 + 512 + 4 + 512
