@@ -136,6 +136,23 @@ KDA_API kda_status kda_prefill_workspace_size(const kda_prefill_desc *d, size_t 
 KDA_API kda_status kda_prefill_chunked(const kda_prefill_desc *d, hipStream_t stream);
 
 /*
+ * The prefill for callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops that must not allocate, harnesses that forbid it.  The same
+ * computation and kernels as kda_prefill_chunked; d->workspace and d->workspace_bytes
+ * are ignored.  The workspace is a fixed array of KDA_NOALLOC_WORKSPACE_BYTES in device
+ * memory, one per GPU, reserved when the library is loaded and held until the process
+ * ends; its device address is looked up on a device's first call.  The call allocates
+ * nothing and needs no zeroed memory (every byte of workspace it reads, it first
+ * writes).  Calls on one GPU share that array: calls that overlap in time on one GPU
+ * (two streams, or two host threads) race and give wrong results; order them.
+ * Errors: as kda_prefill_chunked, and KDA_ERR_WORKSPACE when the descriptor needs more
+ * workspace than the array holds (kda_prefill_workspace_size() bytes; the records take
+ * 61 KiB per 64-token chunk and head).
+ */
+#define KDA_NOALLOC_WORKSPACE_BYTES (64u << 20)
+KDA_API kda_status kda_prefill_chunked_noalloc(const kda_prefill_desc *d, hipStream_t stream);
+
+/*
  * One recurrent decode step ([C]: decode uses the recurrent form; [R]) for N
  * independent sequences and H heads: every state is read and written once, in
  * place.  fp32 arithmetic throughout.

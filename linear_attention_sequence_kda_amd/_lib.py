@@ -83,6 +83,8 @@ def load(path: str = LIB_PATH):
         lib.kda_prefill_workspace_size.restype = C.c_int
         lib.kda_prefill_chunked.argtypes = [C.POINTER(PrefillDesc), vp]
         lib.kda_prefill_chunked.restype = C.c_int
+        lib.kda_prefill_chunked_noalloc.argtypes = [C.POINTER(PrefillDesc), vp]
+        lib.kda_prefill_chunked_noalloc.restype = C.c_int
         lib.kda_decode_step.argtypes = [C.POINTER(DecodeDesc), vp]
         lib.kda_decode_step.restype = C.c_int
         lib.kda_decode_step_pooled.argtypes = [C.POINTER(DecodeDesc), vp, C.c_int32, vp]
@@ -292,6 +294,22 @@ def kda_prefill_chunked(q, k, v, g, beta, *, o, S0=None, S_final=None, gate=None
             workspace = torch.empty(n, dtype=torch.uint8, device=q.device)
     d = _prefill_desc(q, k, v, g, beta, workspace=workspace, **kw)
     _check("kda_prefill_chunked", load().kda_prefill_chunked(C.byref(d), _stream(stream)))
+
+
+# bytes of the fixed device workspace behind kda_prefill_chunked_noalloc (KDA_NOALLOC_WORKSPACE_BYTES)
+NOALLOC_WORKSPACE_BYTES = 64 << 20
+
+
+def kda_prefill_chunked_noalloc(q, k, v, g, beta, *, o, S0=None, S_final=None, gate=None,
+                                norm_weight=None, norm_eps=1e-6, chunk=64, ckpt_every=0,
+                                ckpt=None, n_segments=0, v_split=0, stream=None) -> None:
+    """kda_prefill_chunked without any allocation: the workspace is the library's fixed
+    per-device array of NOALLOC_WORKSPACE_BYTES (calls on one device must not overlap in
+    time).  Raises KdaError with KDA_ERR_WORKSPACE when the call needs more than that."""
+    d = _prefill_desc(q, k, v, g, beta, o=o, S0=S0, S_final=S_final, gate=gate,
+                      norm_weight=norm_weight, norm_eps=norm_eps, chunk=chunk,
+                      ckpt_every=ckpt_every, ckpt=ckpt, n_segments=n_segments, v_split=v_split)
+    _check("kda_prefill_chunked_noalloc", load().kda_prefill_chunked_noalloc(C.byref(d), _stream(stream)))
 
 
 def _decode_desc(q, k, v, g, beta, state, o, gate, norm_weight, norm_eps, pooled=False) -> DecodeDesc:

@@ -1,7 +1,7 @@
 // C ABI of the KDA library: argument validation, execution planning, dispatch.
 // Validation is synchronous and launches nothing on error; every launch is
 // asynchronous on the caller's stream.  No exception crosses the boundary.
-#include <hip/hip_runtime_api.h>
+#include <hip/hip_runtime.h>
 
 #include <atomic>
 #include <cstring>
@@ -240,6 +240,35 @@ kda_status validate_backward(const kda_backward_desc *d, size_t *ws) {
 
 kda_status from_hip(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
 
+// ---------------------------------------------------------------------------
+// the prefill's workspace for callers that cannot allocate: one array in device memory
+// per GPU, reserved when the library is loaded and held until the process ends
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_WORKSPACE_BYTES];
+
+// Device address of `scratch` on each device, looked up once per device with that
+// device current.  In host code `scratch` names a host-side stand-in, never the device
+// memory: only these addresses are passed to kernels.
+std::atomic<void *> g_scratch[kMaxDevices];
+std::atomic<int> g_scratch_state[kMaxDevices];   // 0 not looked up, 1 ok, 2 failed
+
+kda_status scratch_of_current_device(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_DEVICE;
+  int st = g_scratch_state[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e == hipSuccess && p) g_scratch[dev].store(p, std::memory_order_release);
+    st = e == hipSuccess && p ? 1 : 2;
+    // concurrent first calls look up the same address; either store is correct
+    g_scratch_state[dev].store(st, std::memory_order_release);
+  }
+  if (st != 1) return KDA_ERR_HIP;
+  *ptr = g_scratch[dev].load(std::memory_order_acquire);
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -263,6 +292,27 @@ kda_status kda_prefill_chunked(const kda_prefill_desc *d, hipStream_t stream) {
   st = check_device();
   if (st != KDA_OK) return st;
   return from_hip(kda::launch_prefill(*d, p, stream));
+}
+
+kda_status kda_prefill_chunked_noalloc(const kda_prefill_desc *d, hipStream_t stream) {
+  kda_status st = validate_sizes(d);
+  if (st != KDA_OK) return st;
+  PrefillPlan p;
+  st = plan_prefill(*d, &p);
+  if (st != KDA_OK) return st;
+  if (p.ws_total > static_cast<size_t>(KDA_NOALLOC_WORKSPACE_BYTES)) return KDA_ERR_WORKSPACE;
+  if (static_cast<int64_t>(d->B) * d->H == 0) return validate_prefill(d, &p);
+  st = check_device();
+  if (st != KDA_OK) return st;
+  void *ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != KDA_OK) return st;
+  kda_prefill_desc dd = *d;                  // the caller's workspace fields are ignored
+  dd.workspace = ws;
+  dd.workspace_bytes = KDA_NOALLOC_WORKSPACE_BYTES;
+  st = validate_prefill(&dd, &p);
+  if (st != KDA_OK) return st;
+  return from_hip(kda::launch_prefill(dd, p, stream));
 }
 
 kda_status kda_decode_step(const kda_decode_desc *d, hipStream_t stream) {

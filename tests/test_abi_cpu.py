@@ -24,7 +24,8 @@ def test_header_declares_entry_points():
     for n in ("kda_prefill_chunked", "kda_decode_step", "kda_decode_step_pooled",
               "kda_state_checkpoint", "kda_state_rollback", "kda_state_copy_indexed",
               "kda_prefill_workspace_size", "kda_status_string", "kda_abi_version",
-              "kda_prefill_backward", "kda_backward_workspace_size"):
+              "kda_prefill_backward", "kda_backward_workspace_size",
+              "kda_prefill_chunked_noalloc"):
         assert n in names
 
 
@@ -251,3 +252,18 @@ def test_backward_binding_checks_dtypes_and_shapes():
     bad = dict(good, dbeta=torch.zeros(B, T, H, 1))
     with pytest.raises(ValueError, match="dbeta has shape"):
         kda.kda_prefill_backward(q, q, q, g, beta, torch.zeros(B, T, H, 128), **bad)
+
+
+def test_noalloc_refuses_descriptors_beyond_its_array():
+    """kda_prefill_chunked_noalloc checks the workspace its descriptor needs against the
+    fixed device array before touching a device: too large -> KDA_ERR_WORKSPACE; a
+    descriptor that fits gets as far as the device check (no GPU here)."""
+    lib = _lib.load()
+    big = _desc(T=16384, H=8, B=1)                    # 8 x 256 chunk records of 61 KiB > 64 MiB
+    assert lib.kda_prefill_chunked_noalloc(C.byref(big), None) == kda.KDA_ERR_WORKSPACE
+    assert lib.kda_prefill_chunked_noalloc(C.byref(_desc(d_k=64)), None) == kda.KDA_ERR_UNSUPPORTED
+    assert lib.kda_prefill_chunked_noalloc(C.byref(_desc(B=0)), None) == kda.KDA_OK
+    if not _gpu_present():
+        small = _desc()
+        small.workspace, small.workspace_bytes = None, 0   # ignored by this entry point
+        assert lib.kda_prefill_chunked_noalloc(C.byref(small), None) == kda.KDA_ERR_DEVICE
