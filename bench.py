@@ -359,7 +359,11 @@ def main():
         pool = torch.empty((P, Hs, D, D), dtype=torch.float32, device=dev)
         for i in range(0, P, N):                                   # seeded states, 256 at a time
             pool[i:i + N] = up(make_decode_state(N, Hs, D, seed=1 + i // N))
-        slots = torch.from_numpy(np.random.default_rng(1).permutation(P)[:N].astype(np.int32)).to(dev)
+        # four disjoint active batches of N seeded slots, stepped in turn, so that every
+        # step's states come from DRAM as in a serving loop over a large pool
+        perm = np.random.default_rng(1).permutation(P).astype(np.int32)
+        slot_sets = [torch.from_numpy(perm[i * N:(i + 1) * N].copy()).to(dev) for i in range(P // N)]
+        slots = slot_sets[0]
         Xp = make_decode_steps(N, Hs, D, seed=1, steps=16)
         XP = {kk: up(vv) for kk, vv in Xp.items()}
         op = torch.empty((N, Hs, D), dtype=torch.float32, device=dev)
@@ -367,9 +371,10 @@ def main():
 
         def pstep():
             j = ctr[0] % 16
+            sl = slot_sets[ctr[0] % len(slot_sets)]
             ctr[0] += 1
             kda.kda_decode_step_pooled(XP["q"][j], XP["k"][j], XP["v"][j], XP["g"][j], XP["beta"][j],
-                                       pool, slots, o=op, stream=stream)
+                                       pool, sl, o=op, stream=stream)
 
         us = timed(pstep, steps, 5) * 1e3
         db = decode_alg_bytes(N, Hs) + N * 4
@@ -378,7 +383,8 @@ def main():
         wb_ms = timed(lambda: kda.kda_state_copy_indexed(host, pool, src_slots=slots, stream=stream), 3, 1)
         out["decode_pooled"] = {
             "workload": f"decode over a pool of {P} sequences x H={Hs} (fp32 states, 1 GiB), "
-                        f"{N} active sequences at seeded slots, {steps} steps",
+                        f"{N} active sequences at seeded slots, {steps} steps over four disjoint "
+                        "active batches in turn (states from DRAM)",
             "seq_steps_per_s": round(N / (us * 1e-6), 1),
             "us_per_step": round(us, 2),
             "roofline": _roofline(db, us * 1e-3, kernel="decode_kernel (pooled)"),

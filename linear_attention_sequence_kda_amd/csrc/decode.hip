@@ -12,6 +12,13 @@
 // Thread layout (256 threads): column group cg = tid % 32 owns columns 4cg..4cg+3;
 // row phase rp = tid / 32 owns rows rp, rp+8, ..., rp+120 (16 rows).
 //
+// The state is read and written with non-temporal accesses: a decode step streams every
+// state once, so caching it only displaces other lines.  Measured on MI355X with the
+// states of four 256-sequence x 16-head batches stepped in turn (each step's 256 MiB
+// read from DRAM): 92.7 us per step with non-temporal loads and stores against 107.0 us
+// with ordinary ones (5.87 against 5.09 TB/s of algorithmic traffic); non-temporal loads
+// alone give 102.3 us, stores alone 109.5 us.
+//
 // Pooled form (serving): the states live in a pool of slots and sequence n of the
 // batch uses slot slots[n]; everything else is as above.  A slot outside the pool
 // leaves the pool untouched and gives NaN outputs for that sequence.
@@ -23,6 +30,7 @@ namespace {
 
 constexpr int D = 128;
 constexpr int NT = 256;
+typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int ROWS_PER_T = D / 8;   // 16 rows per thread
 
 struct DecodeArgs {
@@ -59,8 +67,10 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
   // Issue the 16 state loads first so their latency overlaps the small vector loads.
   float4 s[ROWS_PER_T];
 #pragma unroll
-  for (int m = 0; m < ROWS_PER_T; ++m)
-    s[m] = *reinterpret_cast<const float4 *>(S + (size_t)(rp + 8 * m) * D + 4 * cg);
+  for (int m = 0; m < ROWS_PER_T; ++m) {
+    const v4f w = __builtin_nontemporal_load(reinterpret_cast<const v4f *>(S + (size_t)(rp + 8 * m) * D + 4 * cg));
+    s[m] = make_float4(w.x, w.y, w.z, w.w);
+  }
 
   if (tid < D) {
     const size_t i = nh * D + tid;
@@ -106,7 +116,7 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
     const float kk = s_k[i];
     float4 x = s[m];
     x.x += kk * u.x; x.y += kk * u.y; x.z += kk * u.z; x.w += kk * u.w;
-    *reinterpret_cast<float4 *>(S + (size_t)i * D + 4 * cg) = x;
+    __builtin_nontemporal_store(v4f{x.x, x.y, x.z, x.w}, reinterpret_cast<v4f *>(S + (size_t)i * D + 4 * cg));
   }
 
   float4 o = make_float4(r[4] + u.x * kq, r[5] + u.y * kq, r[6] + u.z * kq, r[7] + u.w * kq);
