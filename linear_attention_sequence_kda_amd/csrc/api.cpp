@@ -78,9 +78,19 @@ kda_status plan_prefill(const kda_prefill_desc &d, PrefillPlan *p) {
   const size_t dkdv = static_cast<size_t>(d.d_k) * d.d_v;
   p->ws_rec = static_cast<size_t>(units) * static_cast<size_t>(n_chunks) *
               kda::prefill_record_bytes(d.chunk, d.in_dtype == KDA_F32);
+  p->scan_grp = p->n_seg;
   if (p->n_seg > 1) {
     p->ws_maps = static_cast<size_t>(units) * p->n_seg * dkdv * 2 * sizeof(float);
     p->ws_sin = static_cast<size_t>(units) * p->n_seg * dkdv * sizeof(float);
+    // from 32 segments on, the scan runs in groups of about sqrt(n_seg) segments:
+    // 3 (m - 1) dependent map applications instead of n_seg - 1
+    if (p->n_seg >= 32) {
+      int m = 1;
+      while (m * m < p->n_seg) ++m;
+      const int groups = (p->n_seg + m - 1) / m;
+      p->scan_grp = m;
+      p->ws_gmaps = static_cast<size_t>(units) * (groups - 1) * dkdv * 2 * sizeof(float);
+    }
   }
   if (p->split_norm && d.out_dtype == KDA_BF16)
     p->ws_norm = static_cast<size_t>(units) * static_cast<size_t>(d.T) * d.d_v * sizeof(float);
@@ -88,7 +98,8 @@ kda_status plan_prefill(const kda_prefill_desc &d, PrefillPlan *p) {
   p->off_rec = 0;
   p->off_maps = p->off_rec + up(p->ws_rec);
   p->off_sin = p->off_maps + up(p->ws_maps);
-  p->off_norm = p->off_sin + up(p->ws_sin);
+  p->off_gmaps = p->off_sin + up(p->ws_sin);
+  p->off_norm = p->off_gmaps + up(p->ws_gmaps);
   p->ws_total = p->off_norm + up(p->ws_norm);
   return KDA_OK;
 }

@@ -30,8 +30,10 @@ struct PrefillPlan {
   size_t ws_rec;    // bytes: per-chunk records [B,H,n_chunks] written by the prep kernel
   size_t ws_maps;   // bytes: segment maps [B,H,n_seg,d_k,2*d_v] fp32
   size_t ws_sin;    // bytes: states entering each segment [B,H,n_seg,d_k,d_v] fp32
+  int scan_grp;     // segments per group of the scan (n_seg: a single chain)
+  size_t ws_gmaps;  // bytes: composed maps of the scan's groups [B,H,groups-1,d_k,2 d_v] fp32
   size_t ws_norm;   // bytes: raw fp32 outputs [B,T,H,d_v] for the separate norm pass (bf16 out)
-  size_t off_rec, off_maps, off_sin, off_norm;   // byte offsets in the workspace
+  size_t off_rec, off_maps, off_sin, off_gmaps, off_norm;   // byte offsets in the workspace
   size_t ws_total;
 };
 

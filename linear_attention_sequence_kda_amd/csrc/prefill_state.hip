@@ -645,41 +645,68 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// associative scan of segment maps: S_in[0] = S0, S_in[s+1] = A_s S_in[s] + B_s
-// ("xhh.club" structure entry: context parallelism by an associative prefix scan; the
-// states entering later segments are composed, never summed).  One workgroup per
-// (sequence, head, 16-column block); the map product runs as fp32 MFMA.  The eight
-// column blocks of a unit share an XCD (ids equal modulo 8), so each map is fetched
+// Associative scan of segment maps ("xhh.club" structure entry: context parallelism by
+// an associative prefix scan; the states entering later segments are composed, never
+// summed).  A segment map is S -> A S + B, stored [D][2D] as [A | B]; two maps compose
+// as (A2, B2) o (A1, B1) = (A2 A1, A2 B1 + B2).
+//
+// map_chain runs chains of map applications in parallel.  A chain starts from a block
+// X of 16 columns (of a state, or of a map [A | B]) and applies its maps in order,
+// X <- A_j X (+ B_j's matching columns for state columns and for the B part of a map).
+// With n segments the states entering them come from three launches of it (n >= 32:
+// 3 (m - 1) dependent steps instead of n - 1, groups of m ~ sqrt(n) segments):
+//   1. compose:  the maps of every group but the last, composed in parallel per group
+//   2. groups:   S_in at the first segment of every group, one chain over the group maps
+//   3. within:   S_in at every other segment, one chain per group from its first state
+// and from one launch of the third kind over a single group for smaller n.
+//
+// One workgroup per (chain, 16-column block); the map product runs as fp32 MFMA.  The
+// column blocks of a chain share an XCD (ids equal modulo 8), so each map is fetched
 // from memory once into that XCD's L2.  The next map's rows are loaded while the
-// current product runs; each 16x16 result tile accumulates in four independent
-// chains over the 128-long contraction.
+// current product runs; each 16x16 result tile accumulates in four independent chains
+// over the 128-long contraction.
 // ---------------------------------------------------------------------------
 struct MapRows {
   float4 a[2][8];     // A rows (2 tiles), contraction 32lg .. 32lg + 31
   float b[2][4];      // B at rows 4lg + r of each tile, this lane's column
 };
 
+struct ChainArgs {
+  const float *maps;            // [D][2D] maps: step j of chain (bh, g) reads the map at
+                                // maps + bh * map_bh + g * map_grp + map_off + j * D * 2D
+  const float *x0;              // the chain's first block: x0 + bh * x0_bh + g * x0_grp (row
+                                // stride x0_ld), or null for zeros
+  float *out;                   // the block after step j at out + bh * out_bh + g * out_grp +
+                                // (j + 1) * out_step (row stride out_ld); with store_all = 0
+                                // only the last step's block, at out + bh * out_bh + g * out_grp
+  int64_t map_bh, map_grp, map_off, x0_bh, x0_grp, out_bh, out_grp, out_step;
+  int x0_ld, out_ld;
+  int n_bh, n_grp;              // chains: n_bh x n_grp
+  int grp_len, n_total;         // chain g applies min(grp_len, n_total - g grp_len) - 1 maps
+  int ncb;                      // column blocks per chain: 8 (a state) or 16 (a map, A then B)
+  int store_x0, store_all;      // store the first block too (at the chain's output base)
+};
+
 // (no __restrict__ on the maps: with it the compiler sinks the prefetch loads of the
 // next map to their uses, exposing their latency at every step)
-__global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *maps, const float *S0, float *sin,
-                                                           int n_seg, int n_bh) {
-  __shared__ __align__(16) float sXt[2][16][D + 4];   // state block, transposed [n][i], double buffered
+__global__ __launch_bounds__(NTHREADS, 1) void map_chain(ChainArgs a) {
+  __shared__ __align__(16) float sXt[2][16][D + 4];   // the block, transposed [n][i], double buffered
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
-  const int cb = rest % (D / 16), bh = (rest / (D / 16)) * 8 + xcd;
-  if (bh >= n_bh) return;
+  const int cb = rest % a.ncb, chain = (rest / a.ncb) * 8 + xcd;
+  if (chain >= a.n_bh * a.n_grp) return;
+  const int bh = chain / a.n_grp, g = chain % a.n_grp;
+  const int steps = min(a.grp_len, a.n_total - g * a.grp_len) - 1;
   const int c0 = cb * 16;
-  // S_in[0] = S0 (or zeros)
-  for (int x = tid; x < 16 * D; x += NTHREADS) {
-    const int i = x / 16, n = x % 16;
-    const float v = S0 ? S0[(size_t)bh * D * D + (size_t)i * D + c0 + n] : 0.f;
-    sXt[0][n][i] = v;
-    sin[((size_t)bh * n_seg) * D * D + (size_t)i * D + c0 + n] = v;
-  }
+  const bool add_b = a.ncb == 8 || cb >= 8;            // state columns, or the B part of a map
+  const int bcol = D + (cb & 7) * 16;
+  const float *map0 = a.maps + bh * a.map_bh + g * a.map_grp + a.map_off;
+  const float *x0 = a.x0 ? a.x0 + bh * a.x0_bh + g * a.x0_grp + c0 : nullptr;
+  float *out0 = a.out + bh * a.out_bh + g * a.out_grp + c0;
   // wave w computes rows 32w .. 32w + 31 (two 16-row tiles)
-  auto load_map = [&](MapRows &m, int s) __attribute__((always_inline)) {
-    const float *A = maps + ((size_t)bh * n_seg + s) * D * (2 * D);
+  auto load_map = [&](MapRows &m, int j) __attribute__((always_inline)) {
+    const float *A = map0 + (size_t)j * D * (2 * D);
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int row0 = (2 * wave + it) * 16;
@@ -687,19 +714,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *maps, c
 #pragma unroll
       for (int q4 = 0; q4 < 8; ++q4) m.a[it][q4] = *reinterpret_cast<const float4 *>(arow + 4 * q4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) m.b[it][r] = A[(size_t)(row0 + 4 * lg + r) * (2 * D) + D + c0 + lr];
+      for (int r = 0; r < 4; ++r) m.b[it][r] = add_b ? A[(size_t)(row0 + 4 * lg + r) * (2 * D) + bcol + lr] : 0.f;
     }
   };
   // Two map buffers in fixed roles per half of the unrolled loop (no register copies
   // between them), so that the waits for one map's rows do not cover the loads of the
   // next one.
   MapRows m0, m1;
-  if (n_seg > 1) load_map(m0, 0);
+  if (steps > 0) load_map(m0, 0);                      // in flight while the first block loads
+  for (int x = tid; x < 16 * D; x += NTHREADS) {
+    const int i = x / 16, n = x % 16;
+    const float v = x0 ? x0[(size_t)i * a.x0_ld + n] : 0.f;
+    sXt[0][n][i] = v;
+    if (a.store_x0) out0[(size_t)i * a.out_ld + n] = v;
+  }
+  if (steps <= 0) return;                              // the whole workgroup leaves
   __syncthreads();
-  auto step = [&](MapRows &cur, MapRows &nxt, int s) __attribute__((always_inline)) {
+  auto step = [&](MapRows &cur, MapRows &nxt, int j) __attribute__((always_inline)) {
     // unconditional (the last step reloads the last map), so that the compiler's waits
     // for cur count exactly the loads issued after it
-    load_map(nxt, min(s + 1, n_seg - 2));
+    load_map(nxt, min(j + 1, steps - 1));
     f32x4 res[2];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -707,7 +741,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *maps, c
 #pragma unroll
       for (int q4 = 0; q4 < 8; ++q4) {
         const float4 av = cur.a[it][q4];
-        const float4 bv = *reinterpret_cast<const float4 *>(&sXt[s & 1][lr][32 * lg + 4 * q4]);
+        const float4 bv = *reinterpret_cast<const float4 *>(&sXt[j & 1][lr][32 * lg + 4 * q4]);
         c[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, c[0], 0, 0, 0);
         c[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, c[1], 0, 0, 0);
         c[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, c[2], 0, 0, 0);
@@ -716,14 +750,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *maps, c
 #pragma unroll
       for (int r = 0; r < 4; ++r) res[it][r] = ((c[0][r] + c[1][r]) + (c[2][r] + c[3][r])) + cur.b[it][r];
     }
-    float *dst = sin + ((size_t)bh * n_seg + s + 1) * D * D;
+    const bool st = a.store_all || j == steps - 1;
+    float *dst = out0 + (a.store_all ? (j + 1) * a.out_step : 0);
 #pragma unroll
     for (int it = 0; it < 2; ++it)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = (2 * wave + it) * 16 + 4 * lg + r;
-        sXt[(s + 1) & 1][lr][i] = res[it][r];   // the other buffer: no wait for readers of this one
-        dst[(size_t)i * D + c0 + lr] = res[it][r];
+        sXt[(j + 1) & 1][lr][i] = res[it][r];   // the other buffer: no wait for readers of this one
+        if (st) dst[(size_t)i * a.out_ld + lr] = res[it][r];
       }
     // the new block visible to all waves; a barrier without a memory fence, so that the
     // global stores of the block are not waited for
@@ -732,10 +767,54 @@ __global__ __launch_bounds__(NTHREADS, 1) void segment_scan(const float *maps, c
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
-  for (int s = 0; s + 1 < n_seg; s += 2) {
-    step(m0, m1, s);
-    if (s + 2 < n_seg) step(m1, m0, s + 1);
+  for (int j = 0; j < steps; j += 2) {
+    step(m0, m1, j);
+    if (j + 1 < steps) step(m1, m0, j + 1);
   }
+}
+
+hipError_t launch_chain(const ChainArgs &a, hipStream_t s) {
+  const int64_t chains = (int64_t)a.n_bh * a.n_grp;
+  const unsigned grid = static_cast<unsigned>((chains + 7) / 8 * 8 * a.ncb);
+  hipLaunchKernelGGL(map_chain, dim3(grid), dim3(NTHREADS), 0, s, a);
+  return hipGetLastError();
+}
+
+// The states entering every segment: sin[bh][s] for s < n_seg, from the maps of
+// segments 0..n_seg-2 and S0 (null: zeros).  gmaps: workspace for the group maps when
+// grp_len < n_seg, [n_bh][n_seg / grp_len rounded up - 1][D][2D].
+hipError_t segment_scan(const float *maps, const float *S0, float *sin, float *gmaps, int n_seg,
+                        int grp_len, int n_bh, hipStream_t s) {
+  const int64_t DD = (int64_t)D * D, D2D = (int64_t)D * 2 * D;
+  const int G = (n_seg + grp_len - 1) / grp_len;
+  ChainArgs w{};                                       // within groups (or the only chain)
+  w.maps = maps; w.map_bh = n_seg * D2D; w.map_grp = grp_len * D2D; w.map_off = 0;
+  w.out = sin; w.out_bh = n_seg * DD; w.out_grp = grp_len * DD; w.out_step = DD;
+  w.out_ld = D; w.x0_ld = D;
+  w.n_bh = n_bh; w.n_grp = G; w.grp_len = grp_len; w.n_total = n_seg;
+  w.ncb = D / 16; w.store_all = 1;
+  if (G == 1) {
+    w.x0 = S0; w.x0_bh = DD; w.store_x0 = 1;
+    return launch_chain(w, s);
+  }
+  ChainArgs c{};                                       // compose the maps of groups 0..G-2
+  c.maps = maps; c.map_bh = n_seg * D2D; c.map_grp = grp_len * D2D; c.map_off = D2D;
+  c.x0 = maps; c.x0_bh = n_seg * D2D; c.x0_grp = grp_len * D2D; c.x0_ld = 2 * D;
+  c.out = gmaps; c.out_bh = (G - 1) * D2D; c.out_grp = D2D; c.out_ld = 2 * D;
+  c.n_bh = n_bh; c.n_grp = G - 1; c.grp_len = grp_len; c.n_total = (G - 1) * grp_len;
+  c.ncb = 2 * D / 16; c.store_x0 = 0; c.store_all = 0;
+  hipError_t e = launch_chain(c, s);
+  if (e != hipSuccess) return e;
+  ChainArgs q{};                                       // states entering the groups
+  q.maps = gmaps; q.map_bh = (G - 1) * D2D;
+  q.x0 = S0; q.x0_bh = DD; q.x0_ld = D;
+  q.out = sin; q.out_bh = n_seg * DD; q.out_step = grp_len * DD; q.out_ld = D;
+  q.n_bh = n_bh; q.n_grp = 1; q.grp_len = G; q.n_total = G;
+  q.ncb = D / 16; q.store_x0 = 1; q.store_all = 1;
+  e = launch_chain(q, s);
+  if (e != hipSuccess) return e;
+  w.x0 = sin; w.x0_bh = n_seg * DD; w.x0_grp = grp_len * DD; w.store_x0 = 0;
+  return launch_chain(w, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -860,10 +939,8 @@ hipError_t launch_prefill(const kda_prefill_desc &d, const PrefillPlan &p, hipSt
     e = launch_mode<MODE_TRANSITION>(t, d.chunk, f32, 2 * D, s);
     if (e != hipSuccess) return e;
     // pass 2: states entering each segment
-    const unsigned grid = static_cast<unsigned>((units + 7) / 8 * 8 * (D / 16));
-    hipLaunchKernelGGL(segment_scan, dim3(grid), dim3(NTHREADS), 0, s, maps, d.S0, sin, p.n_seg,
-                       static_cast<int>(units));
-    e = hipGetLastError();
+    float *gmaps = p.ws_gmaps ? reinterpret_cast<float *>(ws + p.off_gmaps) : nullptr;
+    e = segment_scan(maps, d.S0, sin, gmaps, p.n_seg, p.scan_grp, static_cast<int>(units), s);
     if (e != hipSuccess) return e;
   }
   // pass 3 (or the single pass): outputs, checkpoints, final state

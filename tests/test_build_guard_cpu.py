@@ -30,7 +30,7 @@ def test_resource_table_lists_the_exact_wait_kernels(tmp_path):
     r = subprocess.run(cmd, capture_output=True, text=True, check=True)
     res = B.check_no_scratch("prefill_state.hip", r.stderr)
     names = " ".join(res)
-    assert "chunk_state_kernel" in names and "segment_scan" in names
+    assert "chunk_state_kernel" in names and "map_chain" in names
     assert all(v["scratch"] == 0 and v["vgpr"] > 0 for v in res.values())
 
 

@@ -274,3 +274,13 @@ def test_large_magnitudes(plan):
     c = _scaled_values(c, 3.0, np.log10(3e4), 1e3, seed=97)
     assert 2e4 < np.max(np.abs(to_f64(c.v, BF16))) <= 3.01e4
     check(c, f"large magnitudes {plan}", **plan)
+
+
+# ---------------------------------------------------------------------------
+# the scan in groups (32 segments or more): compose within groups, chain the group
+# maps, apply within groups; group counts that do not divide the segment count
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("T,n_seg", [(64 * 33, 33), (64 * 45 - 10, 45), (64 * 64, 64), (64 * 130, 130)])
+def test_segments_grouped_scan(T, n_seg):
+    c = make_prefill(1, T, 2, 128, seed=57 + n_seg, in_dtype=BF16, s0_std=0.05)
+    check(c, f"grouped scan, {n_seg} segments", chunk=64, n_segments=n_seg, ckpt_every=256)
