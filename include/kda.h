@@ -88,8 +88,16 @@ typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
  * Numerics.  in_dtype = KDA_BF16: the 16-token diagonal tiles of the intra-chunk
  * products run as BF16 MFMA (operands split into bf16 high and low parts), the
  * remaining products as fp16 MFMA, all with fp32 accumulation; the state is kept
- * in fp32.  The fp16 operands are the v values, the state copy and quantities
- * bounded by |q|, |k|, |v| and |S|: they must stay below 65504 in magnitude.
+ * in fp32.  fp16 ends at 65504 while bf16 values and the fp32 state reach far
+ * beyond it: the operands that carry values (v, the state copy and the delta-rule
+ * update u) are scaled, per 16 state columns and chunk, by a power of two that
+ * keeps their largest magnitude below 2^9 (scale 1, no effect, while everything
+ * is already below), and results are scaled back; any finite bf16 v and fp32 S0
+ * give finite results with the same relative accuracy (tested up to |v| ~ 3e6 and
+ * |S0| ~ 1e6).  The other fp16 operands are built from q, k, g and beta alone and
+ * are bounded by 1 when q and k have unit L2 norm per head and token, as the
+ * method prescribes (beta in [0, 1]); inputs that violate this are outside the
+ * supported range, not detected, and may overflow.
  * in_dtype = KDA_F32: every product runs as fp32 MFMA.
  */
 typedef struct kda_prefill_desc {

@@ -103,6 +103,8 @@ __device__ __forceinline__ void load_v(VRaw<C, NC, F32, MODE> &r, const StateArg
   }
 }
 
+// fp32 values are stored as they are; bf16 values as their bf16 bits, which each wave
+// turns into fp16 operands with the scale of its columns (see the state kernel)
 template <int C, int NC, bool F32, int MODE>
 __device__ __forceinline__ void store_v(typename Op<F32>::T *sV, const VRaw<C, NC, F32, MODE> &r, int nval,
                                         int tid) {
@@ -113,10 +115,15 @@ __device__ __forceinline__ void store_v(typename Op<F32>::T *sV, const VRaw<C, N
     const int x = tid + u * VR::NTH;
     if (VR::NVG % VR::NTH == 0 || x < VR::NVG) {
       const Q8<F32> q = keep_if<F32>(r.v[u], x / per_tok < nval);
-      float vv[8];
+      if constexpr (F32) {
+        float vv[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vv[e] = q8_at<F32>(q, e);
-      st8<F32, VR::VC>(sV, x / per_tok, (x % per_tok) * 8, vv);
+        for (int e = 0; e < 8; ++e) vv[e] = q8_at<F32>(q, e);
+        st8<F32, VR::VC>(sV, x / per_tok, (x % per_tok) * 8, vv);
+      } else {
+        using S = Swz<typename Op<F32>::T, VR::VC>;
+        *reinterpret_cast<uint4 *>(sV + S::at(x / per_tok, (x % per_tok) * 8)) = q;
+      }
     }
   }
 }
@@ -176,6 +183,32 @@ struct SeqFrags {
   static constexpr int n = seq.n;
 };
 
+// Largest of a non-negative float (given as its bits, which order as the values do)
+// over the wave: within rows of 16 lanes by DPP (pairs, quads, half rows, rows), then
+// the four row results through scalar registers.  All 64 lanes must be active.
+__device__ __forceinline__ int wave_max_nonneg(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xf, 0xf, false));    // quad_perm 1,0,3,2
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xf, 0xf, false));    // quad_perm 2,3,0,1
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x141, 0xf, 0xf, false));   // row_half_mirror
+  v = max(v, __builtin_amdgcn_update_dpp(0, v, 0x140, 0xf, 0xf, false));   // row_mirror
+  return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+             max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Operand range.  With bf16 inputs the values, the state copy and U enter the products
+// as fp16 operands, whose range ends at 65504, while bf16 values and the fp32 state can
+// be far larger.  Every product is linear in (values, state) column by column, so each
+// 16-column block of a wave carries a power-of-two scale 2^-e: the fp32 state is held
+// as S 2^-e, values enter as v 2^-e, and outputs, checkpoints, final states and maps
+// are multiplied back by 2^e.  e is 0 (no scaling at all) while every |S| and |v| of the
+// block stays below 2^9; otherwise each step sets it so that the block's largest
+// magnitude lies in [2^8, 2^9).  The bound that makes this enough: for keys of unit
+// norm, beta in [0, 1] and decays at most 1, one token changes a state column's 2-norm
+// by at most |v| (I - beta k k^T has norm at most 1), and |u| is at most |v| plus that
+// norm.  Over a chunk of 64 from entries below 2^9 this gives |u| and |S| below
+// 2^9 (1 + 128^(1/2) + 63) < 38600, inside fp16, and the same argument bounds every
+// record entry (W, T, P, Kdec, Q~) by 1.  Powers of two change no rounding.
+//
 // GATE: the output pass of a whole head (NC = 128) with the fused RMSNorm and gate
 template <int C, int NC, bool F32, int MODE, bool GATE>
 __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(StateArgs a) {
@@ -266,6 +299,12 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
         S[ib][j][r] = x;
       }
     }
+
+  // power-of-two scale exponent of each 16-column block (wave-uniform; always 0 with
+  // fp32 operands)
+  int esc[CBW];
+#pragma unroll
+  for (int j = 0; j < CBW; ++j) esc[j] = 0;
 
   // asynchronous copy of one chunk's record into an LDS buffer: one KiB per wave
   // instruction, lane l's 16 bytes landing at offset 16 l of that KiB (every wave
@@ -385,7 +424,7 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
         for (int j = 0; j < CBW; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            dst[(size_t)(16 * ib + 4 * lg + r) * D + c0 + cw + 16 * j + lr] = S[ib][j][r];
+            dst[(size_t)(16 * ib + 4 * lg + r) * D + c0 + cw + 16 * j + lr] = ldexpf(S[ib][j][r], esc[j]);
     }
   };
 
@@ -463,20 +502,76 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
       __builtin_amdgcn_sched_barrier(0);             // keep the read PF products ahead
       return f;
     };
+    // the A part of a state map (block 0 of each wave) carries no values: no T V product
+    // there
+    auto has_v = [&](int j) __attribute__((always_inline)) { return MODE == MODE_OUTPUT || j == 1; };
     // S and V as operands (contraction over key channels / tokens, split order)
     V8 sf[4][CBW], vf[KB][CBW] = {};
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < CBW; ++j) sf[kb][j] = frag_from<F32>(S[2 * kb][j], S[2 * kb + 1][j]);
-    // the A part of a state map (block 0 of each wave) carries no values: no T V product
-    // there
-    auto has_v = [&](int j) __attribute__((always_inline)) { return MODE == MODE_OUTPUT || j == 1; };
+    if constexpr (F32) {
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-      for (int j = 0; j < CBW; ++j)
-        if (has_v(j)) vf[kb][j] = ld_t_split<F32, VC>(sV, 32 * kb, colb(j) - SH::VOFF - c0, lane);
+        for (int j = 0; j < CBW; ++j)
+          if (has_v(j)) vf[kb][j] = ld_t_split<F32, VC>(sV, 32 * kb, colb(j) - SH::VOFF - c0, lane);
+    } else {
+#pragma unroll
+      for (int j = 0; j < CBW; ++j) {
+        // the largest magnitude of the block's values (bf16 bits in LDS, read again below
+        // once the scale is known, rather than held through the decision)
+        auto vraw = [&](int kb) __attribute__((always_inline)) {
+          // the whole vector reinterpreted: a bit cast of one vector element reads the
+          // vector's first element
+          return __builtin_bit_cast(uint4, ld_t_split<F32, VC>(sV, 32 * kb, colb(j) - SH::VOFF - c0, lane));
+        };
+        uint32_t lmb = 0;                              // as magnitude bits (monotonic)
+        if (has_v(j)) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const uint4 w = vraw(kb);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lmb = max(lmb, max(ww[i] & 0x7fffu, (ww[i] >> 16) & 0x7fffu));
+          }
+        }
+        const float lm = __uint_as_float(lmb << 16);
+        float ls = 0.f;                                // scaled state
+#pragma unroll
+        for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ls = fmaxf(ls, fabsf(S[ib][j][r]));
+        const float lim = 512.f;                       // 2^9
+        if (esc[j] != 0 || __any(lm >= lim || ls >= lim)) {
+          // largest magnitude of the block, in true units, over the wave, and the
+          // exponent en that brings it into [2^8, 2^9)
+          const int mb = wave_max_nonneg(max(__float_as_int(ldexpf(ls, esc[j])), __float_as_int(lm)));
+          const int en = mb >= 0x44000000 ? min(((mb >> 23) & 0xff) - 135, 200) : 0;
+          if (en != esc[j]) {
+#pragma unroll
+            for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) S[ib][j][r] = ldexpf(S[ib][j][r], esc[j] - en);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) sf[kb][j] = frag_from<F32>(S[2 * kb][j], S[2 * kb + 1][j]);
+            esc[j] = en;
+          }
+        }
+        if (has_v(j)) {
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb) {
+            const uint4 w = vraw(kb);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float x = q8_at<false>(w, e);
+              vf[kb][j][e] = Op<F32>::cvt(esc[j] ? ldexpf(x, -esc[j]) : x);
+            }
+          }
+        }
+      }
+    }
 
     // The products run as independent accumulation chains, one per output tile, stepped
     // together over the contraction blocks, so that consecutive MFMAs do not wait on
@@ -565,6 +660,14 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
       for (int tb = 0; tb < NT; ++tb)
 #pragma unroll
         for (int j = 0; j < CBW; ++j) op[tb][j] = O[tb][j];
+#pragma unroll
+      for (int j = 0; j < CBW; ++j)
+        if (esc[j] != 0) {                             // outputs in true units
+#pragma unroll
+          for (int tb = 0; tb < NT; ++tb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) op[tb][j][r] = ldexpf(op[tb][j][r], esc[j]);
+        }
     }
     // per-token sums of squares of this wave's columns for the fused RMSNorm
     if constexpr (GATE) {
@@ -575,7 +678,7 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
 #pragma unroll
         for (int j = 0; j < CBW; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) ss += O[tb][j][r] * O[tb][j][r];
+          for (int r = 0; r < 4; ++r) ss += op[tb][j][r] * op[tb][j][r];   // true units
         ss += __shfl_xor(ss, 16, 64);
         ss += __shfl_xor(ss, 32, 64);
         if (lg == 0) sn[(16 * tb + lr) * NW + wave] = ss;
@@ -627,7 +730,7 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
         for (int j = 0; j < CBW; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            a.S_final[state_off + (size_t)(16 * ib + 4 * lg + r) * D + c0 + cw + 16 * j + lr] = S[ib][j][r];
+            a.S_final[state_off + (size_t)(16 * ib + 4 * lg + r) * D + c0 + cw + 16 * j + lr] = ldexpf(S[ib][j][r], esc[j]);
     }
   } else {
     float *dst = a.maps + (size_t)unit * D * (2 * D);
@@ -637,7 +740,7 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
       for (int j = 0; j < CBW; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          dst[(size_t)(16 * ib + 4 * lg + r) * (2 * D) + colb(j) + lr] = S[ib][j][r];
+          dst[(size_t)(16 * ib + 4 * lg + r) * (2 * D) + colb(j) + lr] = ldexpf(S[ib][j][r], esc[j]);
   }
   // the copies of the last iteration (a reload of the last chunk) complete before the
   // workgroup's LDS is released

@@ -276,6 +276,55 @@ def test_large_magnitudes(plan):
     check(c, f"large magnitudes {plan}", **plan)
 
 
+@pytest.mark.parametrize("plan", [dict(chunk=64), dict(chunk=64, n_segments=3, ckpt_every=128),
+                                  dict(chunk=16, gate=True), dict(chunk=64, v_split=2, gate=True),
+                                  dict(chunk=64, gate=True), dict(chunk=64, n_segments=40, ckpt_every=64)],
+                         ids=["c64", "c64-seg3-ckpt", "c16-gate", "c64-vsplit2-gate", "c64-gate",
+                              "c64-seg40-ckpt"])
+def test_beyond_fp16_range(plan):
+    """Rows of v with largest magnitudes from 1e5 to 3e6 and S0 entries ~1e5: bf16 holds
+    them, fp16 (max 65504) does not.  Each 16-column block of the state pass carries a
+    power-of-two scale, so the results are finite and meet the same parity bound."""
+    T = 64 * 41 if plan.get("n_segments", 0) > 32 else 650
+    c = make_prefill(2, T, 2, 128, seed=131, in_dtype=BF16, s0_std=1.0, gate=plan.get("gate", False))
+    c = _scaled_values(c, 5.0, np.log10(3e6), 1e5, seed=131)
+    assert np.max(np.abs(to_f64(c.v, BF16))) > 65504 and np.max(np.abs(c.S0)) > 65504
+    o, S = check(c, f"beyond fp16 range {plan}", **plan)
+    assert np.isfinite(down(S)).all()
+
+
+def test_mixed_magnitudes_per_head():
+    """One head at unit scale beside one at 1e6: the scale is per block of columns and
+    per head, so the small head loses nothing (errors measured head by head)."""
+    c = make_prefill(1, 300, 2, 128, seed=141, in_dtype=BF16, s0_std=0.05)
+    v = to_f64(c.v, BF16)
+    v[:, :, 1] *= 1e6
+    c.v = f32_to_bf16(v.astype(np.float32))
+    S0 = c.S0.astype(np.float64)
+    S0[:, 1] *= 1e6
+    c.S0 = S0.astype(np.float32)
+    o, S, _ = run_gpu(c, chunk=64, n_segments=2)
+    o_ref, S_ref, _ = run_ref(c)
+    og, Sg = down(o), down(S)
+    for h in range(2):
+        eo, es = err_o(og[:, :, h], o_ref[:, :, h]), err_S(Sg[:, h], S_ref[:, h])
+        _say(f"mixed magnitudes, head {h}: err_o={eo:.3e} err_S={es:.3e}")
+        assert eo <= TOL_O_BF16 and es <= TOL_S_BF16, (h, eo, es)
+
+
+def test_scale_returns_to_one():
+    """Huge S0 that decays away (g at the floor) while v is at unit scale: the scale
+    drops back to 2^0 once the state is small, and the later outputs keep the
+    accuracy of an unscaled run."""
+    c = make_prefill(1, 640, 1, 128, seed=151, in_dtype=BF16, s0_std=1e6, g_mode="floor")
+    o, S, _ = run_gpu(c, chunk=64)
+    o_ref, S_ref, _ = run_ref(c)
+    og = down(o)
+    eo = err_o(og[:, 128:], o_ref[:, 128:])
+    _say(f"decayed scale: err_o(after 128 tokens)={eo:.3e} err_S={err_S(down(S), S_ref):.3e}")
+    assert eo <= TOL_O_BF16 and err_S(down(S), S_ref) <= TOL_S_BF16
+
+
 # ---------------------------------------------------------------------------
 # the scan in groups (32 segments or more): compose within groups, chain the group
 # maps, apply within groups; group counts that do not divide the segment count
