@@ -520,24 +520,26 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
     } else {
 #pragma unroll
       for (int j = 0; j < CBW; ++j) {
-        // the largest magnitude of the block's values (bf16 bits in LDS, read again below
-        // once the scale is known, rather than held through the decision)
+        // the block's values (bf16 bits in LDS) as unscaled operands, and their largest
+        // magnitude
         auto vraw = [&](int kb) __attribute__((always_inline)) {
           // the whole vector reinterpreted: a bit cast of one vector element reads the
           // vector's first element
           return __builtin_bit_cast(uint4, ld_t_split<F32, VC>(sV, 32 * kb, colb(j) - SH::VOFF - c0, lane));
         };
-        uint32_t lmb = 0;                              // as magnitude bits (monotonic)
+        float lm = 0.f;
         if (has_v(j)) {
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb) {
             const uint4 w = vraw(kb);
-            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) lmb = max(lmb, max(ww[i] & 0x7fffu, (ww[i] >> 16) & 0x7fffu));
+            for (int e = 0; e < 8; ++e) {
+              const float x = q8_at<false>(w, e);
+              lm = fmaxf(lm, fabsf(x));
+              vf[kb][j][e] = Op<F32>::cvt(x);
+            }
           }
         }
-        const float lm = __uint_as_float(lmb << 16);
         float ls = 0.f;                                // scaled state
 #pragma unroll
         for (int ib = 0; ib < 8; ++ib)
@@ -548,7 +550,7 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
           // largest magnitude of the block, in true units, over the wave, and the
           // exponent en that brings it into [2^8, 2^9)
           const int mb = wave_max_nonneg(max(__float_as_int(ldexpf(ls, esc[j])), __float_as_int(lm)));
-          const int en = mb >= 0x44000000 ? min(((mb >> 23) & 0xff) - 135, 200) : 0;
+          const int en = mb >= 0x44000000 ? min(((mb >> 23) & 0xff) - 135, 120) : 0;
           if (en != esc[j]) {
 #pragma unroll
             for (int ib = 0; ib < 8; ++ib)
@@ -558,15 +560,13 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
             for (int kb = 0; kb < 4; ++kb) sf[kb][j] = frag_from<F32>(S[2 * kb][j], S[2 * kb + 1][j]);
             esc[j] = en;
           }
-        }
-        if (has_v(j)) {
+          if (has_v(j) && esc[j] != 0) {               // the values again, scaled
+            const float sc = __int_as_float((127 - esc[j]) << 23);   // 2^-e, e <= 120
 #pragma unroll
-          for (int kb = 0; kb < KB; ++kb) {
-            const uint4 w = vraw(kb);
+            for (int kb = 0; kb < KB; ++kb) {
+              const uint4 w = vraw(kb);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const float x = q8_at<false>(w, e);
-              vf[kb][j][e] = Op<F32>::cvt(esc[j] ? ldexpf(x, -esc[j]) : x);
+              for (int e = 0; e < 8; ++e) vf[kb][j][e] = Op<F32>::cvt(q8_at<false>(w, e) * sc);
             }
           }
         }
