@@ -503,10 +503,28 @@ def main():
         ckt = torch.empty_like(st)
         kda.kda_state_checkpoint(st, ckt, stream=stream)
         us_rb = timed(lambda: kda.kda_state_rollback(st, ckt, stream=stream), 50, 5) * 1e3
-        leg["decode_tail"] = {"us_per_step": round(us_tail, 2), "steps": 64,
-                              "note": "one sequence x 8 heads: 8 workgroups, bound by launch and "
-                                      "memory latency, not bandwidth"}
-        leg["rollback"] = {"us": round(us_rb, 2), "states": H4, "bytes": H4 * D * D * 4}
+        # the same 64 steps, and 16 rollbacks, captured in HIP graphs and replayed: the
+        # device-side cost without one host launch per call (calls made inside the capture
+        # go to the capturing stream)
+        torch.cuda.synchronize()
+        g_tail, g_rb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_tail):
+            for j in range(64):
+                kda.kda_decode_step(Xt["q"][j], Xt["k"][j], Xt["v"][j], Xt["g"][j], Xt["beta"][j], st,
+                                    o=ot)
+        with torch.cuda.graph(g_rb):
+            for _ in range(16):
+                kda.kda_state_rollback(st, ckt)
+        us_tail_g = timed(g_tail.replay, 20, 3) * 1e3 / 64
+        us_rb_g = timed(g_rb.replay, 20, 3) * 1e3 / 16
+        leg["decode_tail"] = {"us_per_step": round(us_tail, 2), "us_per_step_graph": round(us_tail_g, 2),
+                              "steps": 64,
+                              "note": "one sequence x 8 heads, each state split into four 32-column "
+                                      "slices (32 workgroups); us_per_step launches every step from the "
+                                      "host, us_per_step_graph replays the 64 steps as one HIP graph"}
+        leg["rollback"] = {"us": round(us_rb, 2), "us_graph": round(us_rb_g, 2), "states": H4,
+                           "bytes": H4 * D * D * 4}
+        del g_tail, g_rb
         out["prefill_1m"] = leg
         del S4, st, ckt, Xt
 

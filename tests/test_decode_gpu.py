@@ -77,6 +77,20 @@ def test_decode_bf16_out():
     assert err_S(S, S_ref) <= 1e-5
 
 
+@pytest.mark.parametrize("N,H", [(1, 8), (17, 15), (16, 16), (9, 29)])
+def test_decode_whole_and_split_states(N, H):
+    """Below 256 states an ungated step splits each state into four 32-column slices,
+    from 256 on a workgroup takes a whole state: both sides of the threshold, state counts
+    that are not a multiple of eight, and the one-sequence x 8-head step of the long
+    prefill's decode tail."""
+    path = "split" if N * H < 256 else "whole"
+    _say(f"decode N={N} H={H} ({N * H} states, {path} path), 8 steps")
+    o, o_ref, S, S_ref = _run_steps(N, H, 8, seed=N * 100 + H)
+    e, es = err_o(o, o_ref), err_S(S, S_ref)
+    _say(f"err_o={e:.3e} err_S={es:.3e}")
+    assert e <= TOL_DECODE and es <= 1e-5
+
+
 def test_decode_workload_shape_sampled():
     """256 sequences x 16 heads, 1000 steps, state N(0, 0.05): all states run on the GPU,
     the oracle follows 64 sampled (sequence, head) pairs through every step."""
