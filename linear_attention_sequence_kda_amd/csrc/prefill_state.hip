@@ -316,8 +316,10 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
 #pragma unroll
     for (int n = n0; n < n1; ++n) {
       const int blk = min(wave + NW * n, NBLK - 1);
+      // non-temporal (cache policy 2): a record is read once per pass, and caching it only
+      // displaces other lines (1% on the 8k workload)
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void *)(src + (uint32_t)(blk * 1024 + 16 * lane)),
-                                       (__attribute__((address_space(3))) void *)(dst + (size_t)blk * 1024), 16, 0, 0);
+                                       (__attribute__((address_space(3))) void *)(dst + (size_t)blk * 1024), 16, 0, 2);
     }
   };
   // gate logits for the fused epilogue: token 16tb + lr, columns cw + 16j + 4lg .. +3
