@@ -115,6 +115,17 @@ def _traffic_from_profiles(kernel_hash):
     return None if v is None else int(v)
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _cores():
     try:
         return len(os.sched_getaffinity(0))
@@ -135,28 +146,28 @@ def cpu_baseline(c, gate):
         norm_gate(o, to_f64(c.gate, "bf16"), 1e-6) if gate else o
         dt += time.perf_counter() - t0
         passes += 1
-    return dict(value=passes * c.B * c.T / dt, unit="tokens/s", cores=threads, kind="oracle",
+    return dict(value=passes * c.B * c.T / dt, unit="tokens/s", cores=threads, cpu_model=_cpu_model(), kind="oracle",
                 sample=f"{passes} passes over the whole prefill workload (B={c.B}, T={c.T}, "
                        f"H={c.H}), fp64 C recurrence + numpy norm/gate, {dt:.1f} s")
 
 
 def decode_cpu_baseline(S_np, X):
     """Time the fp64 C oracle stepping the decode workload (all states, the same step
-    inputs the GPU leg uses) on the host cores, for about 5 s."""
+    inputs the GPU leg uses) on the host cores, for about 10 s."""
     from oracle import native
     threads = max(1, min(_cores(), 64))
     N, H = S_np.shape[:2]
     S = S_np.astype(np.float64)
     nx = X["q"].shape[0]
     steps, dt = 0, 0.0
-    while steps < 200 and (steps < 2 or dt < 5.0):
+    while steps < 3000 and (steps < 2 or dt < 10.0):
         j = steps % nx
         t0 = time.perf_counter()
         native.decode_step(S, X["q"][j], X["k"][j], X["v"][j], X["g"][j], X["beta"][j], bf16=True,
                            nthreads=threads)
         dt += time.perf_counter() - t0
         steps += 1
-    return dict(value=N * steps / dt, unit="seq-steps/s", cores=threads, kind="oracle",
+    return dict(value=N * steps / dt, unit="seq-steps/s", cores=threads, cpu_model=_cpu_model(), kind="oracle",
                 sample=f"{steps} steps of all {N} sequences x {H} heads (fp64 C recurrence), "
                        f"{dt:.1f} s")
 
@@ -296,6 +307,29 @@ def main():
         "workspace_bytes": int(ws_bytes),
     }
 
+    # ---------------- measured HBM ceiling ----------------
+    # A copy of 1 GiB into another 1 GiB buffer (four times the last-level cache, so from
+    # DRAM) with the library's own copy kernel: what a plain streaming kernel reaches on
+    # this box, next to the 8 TB/s of the specification.
+    _say("bench: HBM copy probe")
+    n_pr = 16384                                             # 64 KiB states: 1 GiB
+    pa = torch.ones((n_pr, D, D), dtype=torch.float32, device=dev)
+    pb = torch.empty_like(pa)
+    flip = [0]
+
+    def probe_copy():
+        flip[0] ^= 1
+        src, dst = (pa, pb) if flip[0] else (pb, pa)
+        kda.kda_state_checkpoint(src, dst, stream=stream)
+
+    ms_pr = timed(probe_copy, 10, 3)
+    probe_gbs = 2 * n_pr * D * D * 4 / (ms_pr * 1e-3) / 1e9
+    out["hbm_probe"] = {"what": "1 GiB -> 1 GiB copy with the library's copy kernel (DRAM), "
+                                "read + write bytes over time",
+                        "ms": round(ms_pr, 3), "GB_per_s": round(probe_gbs, 1)}
+    del pa, pb
+    out["roofline"]["frac_of_measured_copy"] = round(out["roofline"]["achieved"] / probe_gbs, 4)
+
     # ---------------- decode workload ----------------
     if not a.no_decode:
         N, Hd, steps = 256, 16, a.decode_steps
@@ -319,6 +353,20 @@ def main():
                                 sets[s % 4], o=od, stream=stream)
 
         us_dram = timed(dstep_sets, steps, 12) * 1e3
+        # per-step distribution: 200 more steps, each between its own pair of events
+        per = []
+        for _ in range(200):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dstep_sets()
+            e1.record(stream)
+            per.append((e0, e1))
+        torch.cuda.synchronize()
+        per = np.sort(np.array([x.elapsed_time(y) * 1e3 for x, y in per]))
+        per_step = {"min": round(float(per[0]), 2), "p50": round(float(np.median(per)), 2),
+                    "p90": round(float(per[int(0.9 * len(per))]), 2), "max": round(float(per[-1]), 2),
+                    "note": "200 steps, each between its own pair of events (an event pair adds "
+                            "about a microsecond)"}
         St = sets[0]
         ctr[0] = 0
 
@@ -337,7 +385,9 @@ def main():
                         "from DRAM",
             "seq_steps_per_s": round(N / (us_dram * 1e-6), 1),
             "us_per_step": round(us_dram, 2),
-            "roofline": _roofline(db, us_dram * 1e-3, kernel="decode_kernel"),
+            "per_step_us": per_step,
+            "roofline": _roofline(db, us_dram * 1e-3, kernel="decode_kernel",
+                                  frac_of_measured_copy=round(db / (us_dram * 1e-6) / 1e9 / probe_gbs, 4)),
         }
         out["decode_in_cache"] = {
             "workload": "the same step on one state set (256 MiB, near the 256 MB last-level "

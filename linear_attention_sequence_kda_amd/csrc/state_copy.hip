@@ -11,11 +11,18 @@
 namespace kda {
 namespace {
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// Non-temporal stores: a copy writes each line once and does not read it back.  With
+// them and at most 1024 workgroups a 1 GiB copy reaches about 6 TB/s on MI355X (5.2 TB/s
+// with ordinary stores and 4096 workgroups).
 __global__ __launch_bounds__(256) void copy_vec4(float4 *__restrict__ dst,
                                                  const float4 *__restrict__ src, int64_t n4) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
-    dst[i] = src[i];
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
+    const float4 v = src[i];
+    __builtin_nontemporal_store(v4f{v.x, v.y, v.z, v.w}, reinterpret_cast<v4f *>(dst + i));
+  }
 }
 
 __global__ __launch_bounds__(256) void copy_scalar(float *__restrict__ dst,
@@ -68,7 +75,7 @@ __global__ __launch_bounds__(256) void copy_indexed_scalar(float *__restrict__ d
 
 unsigned grid_for(int64_t n) {
   const int64_t blocks = (n + 255) / 256;
-  return static_cast<unsigned>(blocks < 4096 ? (blocks < 1 ? 1 : blocks) : 4096);
+  return static_cast<unsigned>(blocks < 1024 ? (blocks < 1 ? 1 : blocks) : 1024);
 }
 
 }  // namespace
