@@ -133,22 +133,64 @@ def _cores():
         return os.cpu_count() or 1
 
 
-def cpu_baseline(c, gate):
-    """Time the fp64 C oracle (plus the numpy norm/gate) on the host cores."""
+def _err_o(x, ref):
+    return float(np.max(np.abs(x - ref)) / np.sqrt(np.mean(ref * ref)))
+
+
+def _err_S(x, ref):
+    return float(np.linalg.norm(x - ref) / np.linalg.norm(ref))
+
+
+def cpu_baseline(c, gate, o_gpu=None, S_gpu=None):
+    """Time the fp64 C oracle (plus the numpy norm/gate) on the host cores; the first
+    pass's outputs also check the GPU outputs of the same run (returned as parity)."""
     from oracle import native, norm_gate
     from kda_inputs import to_f64
     threads = max(1, min(_cores(), 64))
     # whole passes over the workload until about 10 s of wall time (at most 20 passes)
-    passes, dt = 0, 0.0
+    passes, dt, parity = 0, 0.0, None
     while passes < 20 and (passes == 0 or dt < 10.0):
         t0 = time.perf_counter()
         o, S, _ = native.prefill(c.q, c.k, c.v, c.g, c.beta, c.S0, bf16=True, nthreads=threads)
-        norm_gate(o, to_f64(c.gate, "bf16"), 1e-6) if gate else o
+        o = norm_gate(o, to_f64(c.gate, "bf16"), 1e-6) if gate else o
         dt += time.perf_counter() - t0
+        if passes == 0 and o_gpu is not None:
+            parity = dict(err_o=_err_o(o_gpu, o), err_S=_err_S(S_gpu, S),
+                          bound="err_o <= 2e-2, err_S <= 1e-2", compared="every output and final state")
         passes += 1
     return dict(value=passes * c.B * c.T / dt, unit="tokens/s", cores=threads, cpu_model=_cpu_model(), kind="oracle",
                 sample=f"{passes} passes over the whole prefill workload (B={c.B}, T={c.T}, "
-                       f"H={c.H}), fp64 C recurrence + numpy norm/gate, {dt:.1f} s")
+                       f"H={c.H}), fp64 C recurrence + numpy norm/gate, {dt:.1f} s"), parity
+
+
+def prefix_cpu_baseline(pre, T_full, H, ckpt_every, what, o_gpu=None, ck_gpu=None):
+    """Time the fp64 C oracle on a contiguous prefix of a long workload (all heads), for
+    about 5 s, and report its tokens/s: the sequential recurrence costs the same per token,
+    so the rate of the prefix is the rate of the whole (extrapolated, not run whole).  The
+    GPU's outputs (and checkpoints) of those tokens do not depend on later tokens, so the
+    first pass also checks them (returned as parity)."""
+    from oracle import native
+    threads = max(1, min(_cores(), 64))
+    T = pre["q"].shape[1]
+    passes, dt, parity = 0, 0.0, None
+    while passes < 100 and (passes == 0 or dt < 5.0):
+        t0 = time.perf_counter()
+        o, _, ck = native.prefill(pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], None, bf16=True,
+                                  ckpt_every=ckpt_every, nthreads=threads)
+        dt += time.perf_counter() - t0
+        if passes == 0 and o_gpu is not None:
+            parity = dict(err_o=_err_o(o_gpu, o), bound="err_o <= 2e-2, err_S <= 1e-2",
+                          compared=f"every output of the first {T} tokens, all heads")
+            if ck_gpu is not None:
+                parity["err_S_checkpoints"] = max(_err_S(ck_gpu[:, m], ck[:, m]) for m in range(ck.shape[1]))
+                parity["compared"] += f", and their {ck.shape[1]} checkpoints"
+        passes += 1
+    rate = passes * T / dt
+    return dict(value=round(rate, 1), unit="tokens/s", cores=threads, cpu_model=_cpu_model(),
+                kind="oracle", extrapolated=True,
+                sample=f"{passes} passes over the first {T} of {T_full} tokens ({what}, all {H} "
+                       f"heads), fp64 C recurrence, {dt:.1f} s; whole-workload time at this rate "
+                       f"{T_full / rate:.1f} s"), parity
 
 
 def decode_cpu_baseline(S_np, X):
@@ -260,6 +302,9 @@ def main():
     wall = time.perf_counter() - t_start
     ms_mean = e_start.elapsed_time(e_end) / a.steps           # average call duration
     ms_step = wall * 1e3 / a.steps
+    # the outputs of the timed calls, for the parity check against the oracle's pass
+    o_host = o.double().cpu().numpy() if not a.no_cpu_baseline else None
+    S_host = Sf.double().cpu().numpy() if not a.no_cpu_baseline else None
     tokens = B * T
     value = tokens / (ms_step * 1e-3)
     alg_b = table_prefill_bytes(B, T, H, gate=True)
@@ -485,8 +530,8 @@ def main():
 
     if not a.no_cpu_baseline:
         _say("bench: prefill oracle baseline")
-        out["cpu_baseline"] = cpu_baseline(c, gate=True)
-    del q, k, v, g, beta, gate, S0, o, Sf, ws, c
+        out["cpu_baseline"], out["parity"] = cpu_baseline(c, gate=True, o_gpu=o_host, S_gpu=S_host)
+    del q, k, v, g, beta, gate, S0, o, Sf, ws, c, o_host, S_host
 
     # ---------------- long sequences: 131k with checkpoints, 1M over 256 segments ----------------
     if not a.no_long:
@@ -494,6 +539,7 @@ def main():
         c3 = make_workload("prefill_131k", seed=0)
         T3, H3, every = c3.T, c3.H, 512
         t3 = [up(x) for x in (c3.q, c3.k, c3.v, c3.g, c3.beta)]
+        pre3 = {n: np.ascontiguousarray(getattr(c3, n)[:, :8192]) for n in ("q", "k", "v", "g", "beta")}
         del c3
         o3 = torch.empty((1, T3, H3, D), dtype=torch.float32, device=dev)
         S3 = torch.empty((1, H3, D, D), dtype=torch.float32, device=dev)
@@ -512,12 +558,21 @@ def main():
             "mfma_frac": round(prefill_alg_flops(1, T3, H3) / (ms3 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "workspace_bytes": int(ws3.numel()),
         }
+        o3_pre = o3[:, :8192].double().cpu().numpy()
+        ck3_pre = ck3[:, :8192 // every].double().cpu().numpy()
         del t3, o3, S3, ck3, ws3
+        if not a.no_cpu_baseline:
+            _say("bench: 131k oracle baseline (prefix)")
+            (out["prefill_131k"]["cpu_baseline"],
+             out["prefill_131k"]["parity"]) = prefix_cpu_baseline(pre3, T3, H3, every, "checkpoints every 512",
+                                                                  o_gpu=o3_pre, ck_gpu=ck3_pre)
+        del pre3, o3_pre, ck3_pre
 
         _say("bench: 1M prefill")
         c4 = make_workload("prefill_1m", seed=0)
         T4, H4 = c4.T, c4.H
         t4 = [up(x) for x in (c4.q, c4.k, c4.v, c4.g, c4.beta)]
+        pre4 = {n: np.ascontiguousarray(getattr(c4, n)[:, :16384]) for n in ("q", "k", "v", "g", "beta")}
         del c4
         o4 = torch.empty((1, T4, H4, D), dtype=torch.float32, device=dev)
         S4 = torch.empty((1, H4, D, D), dtype=torch.float32, device=dev)
@@ -535,6 +590,7 @@ def main():
             "mfma_frac": round(prefill_alg_flops(1, T4, H4) / (ms4 * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
             "workspace_bytes": int(ws4.numel()),
         }
+        o4_pre = o4[:, :16384].double().cpu().numpy()
         del t4, o4, ws4
         # decode tail: 64 single-token steps of the one sequence from the prefill's final
         # state, then the rollback of its 8 states from a checkpoint
@@ -575,8 +631,12 @@ def main():
         leg["rollback"] = {"us": round(us_rb, 2), "us_graph": round(us_rb_g, 2), "states": H4,
                            "bytes": H4 * D * D * 4}
         del g_tail, g_rb
+        if not a.no_cpu_baseline:
+            _say("bench: 1M oracle baseline (prefix)")
+            leg["cpu_baseline"], leg["parity"] = prefix_cpu_baseline(
+                pre4, T4, H4, 0, "no checkpoints; 4 of the 256 segments", o_gpu=o4_pre)
         out["prefill_1m"] = leg
-        del S4, st, ckt, Xt
+        del S4, st, ckt, Xt, pre4, o4_pre
 
     print(json.dumps(out), flush=True)
 
