@@ -348,6 +348,11 @@ def main():
             "achieved_tflops": round(alg_f / (kernel_ms * 1e-3) / 1e12, 2),
             "peak_tflops": BF16_PEAK_TFLOPS,
             "frac": round(alg_f / (kernel_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            # attainable = min(MFMA peak, arithmetic intensity x HBM peak): HBM-bound here,
+            # so the fraction of it equals the HBM roofline fraction
+            "attainable_tflops": round(min(BF16_PEAK_TFLOPS, alg_f / alg_b * HBM_PEAK_GBS * 1e9 / 1e12), 1),
+            "frac_of_attainable": round(alg_f / (kernel_ms * 1e-3) / 1e12
+                                        / min(BF16_PEAK_TFLOPS, alg_f / alg_b * HBM_PEAK_GBS * 1e9 / 1e12), 4),
         },
         "workspace_bytes": int(ws_bytes),
     }
