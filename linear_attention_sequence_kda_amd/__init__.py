@@ -9,7 +9,7 @@ from ._lib import (  # noqa: F401
     KDA_ERR_ALIAS, KDA_ERR_DEVICE, KDA_ERR_HIP, KDA_F32, KDA_BF16, LIB_PATH, load,
     status_string, kda_abi_version, kda_prefill_workspace_size, kda_prefill_chunked,
     kda_prefill_chunked_noalloc, NOALLOC_WORKSPACE_BYTES,
-    kda_decode_step, kda_decode_step_pooled, kda_state_copy_indexed, kda_state_checkpoint,
+    kda_decode_step, kda_decode_step_pooled, DecodeStep, kda_state_copy_indexed, kda_state_checkpoint,
     kda_state_rollback, kda_backward_workspace_size, kda_prefill_backward, PrefillDesc,
     DecodeDesc, BackwardDesc,
 )

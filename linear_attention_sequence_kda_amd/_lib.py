@@ -342,6 +342,37 @@ def kda_decode_step_pooled(q, k, v, g, beta, pool, slots, *, o, gate=None, norm_
                                          _stream(stream)))
 
 
+class DecodeStep:
+    """kda_decode_step (or, with `slots`, kda_decode_step_pooled) bound to fixed buffers,
+    for loops that refill the same input buffers every step, as a serving loop does: the
+    tensors are checked and the C descriptor is built once, and each call only launches.
+    The object keeps the tensors alive; their contents may change between calls, their
+    storage may not (no resize, no reassignment of the tensors' data).  Calling it runs
+    the same kernel on the same arguments as the one-shot functions, with bit-identical
+    results."""
+
+    def __init__(self, q, k, v, g, beta, state, *, o, gate=None, norm_weight=None,
+                 norm_eps=1e-6, slots=None):
+        self._pooled = slots is not None
+        if self._pooled:
+            _expect("slots", slots, (int(q.shape[0]),), (torch.int32,), q.device)
+        self._d = _decode_desc(q, k, v, g, beta, state, o, gate, norm_weight, norm_eps,
+                               pooled=self._pooled)
+        self._keep = (q, k, v, g, beta, state, o, gate, norm_weight, slots)
+        self._ref = C.byref(self._d)
+        self._lib = load()
+        if self._pooled:
+            self._slots, self._pool = _slots(slots), int(state.shape[0])
+
+    def __call__(self, stream=None) -> None:
+        s = _stream(stream)
+        if self._pooled:
+            st = self._lib.kda_decode_step_pooled(self._ref, self._slots, self._pool, s)
+        else:
+            st = self._lib.kda_decode_step(self._ref, s)
+        _check("kda_decode_step_pooled" if self._pooled else "kda_decode_step", st)
+
+
 def kda_state_copy_indexed(dst, src, *, dst_slots=None, src_slots=None, n=None,
                            stream=None) -> None:
     """dst[dst_slots[i]] = src[src_slots[i]] for i < n (slot i where a slot tensor is None).

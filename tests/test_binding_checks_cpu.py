@@ -160,3 +160,19 @@ def test_indexed_copy_and_checkpoint_checks():
         kda.kda_state_checkpoint(t(2, D, D, dtype=BF), t(2, D, D, dtype=BF))
     with pytest.raises(ValueError, match="shapes differ"):
         kda.kda_state_rollback(t(2, D, D), t(3, D, D))
+
+
+@pytest.mark.parametrize("name,bad,msg", DECODE_BAD[:4], ids=[f"{n}-{m}" for n, _, m in DECODE_BAD[:4]])
+def test_prepared_decode_step_checks_at_construction(name, bad, msg):
+    """DecodeStep checks its buffers once, when it is built (the same checks as the
+    one-shot call), so that each later call only launches."""
+    a = decode_args(**{name: bad})
+    args = [a.pop(n) for n in ("q", "k", "v", "g", "beta", "state")]
+    with pytest.raises(ValueError, match=msg):
+        kda.DecodeStep(*args, **a)
+    a = decode_args()
+    args = [a.pop(n) for n in ("q", "k", "v", "g", "beta", "state")]
+    with pytest.raises(ValueError, match="HIP device"):          # well formed: the device check
+        kda.DecodeStep(*args, **a)
+    with pytest.raises(ValueError, match="slots has dtype"):
+        kda.DecodeStep(*args, slots=t(N, dtype=torch.int64), **a)

@@ -140,3 +140,33 @@ def test_prefix_cache_reuse_from_checkpoint():
     es = err_S(down(S2), S_ref)
     _say(f"prefix reuse: err_o={eo:.3e} err_S={es:.3e}")
     assert eo <= 2e-2 and es <= 1e-2
+
+
+@pytest.mark.parametrize("pooled", [False, True], ids=["plain", "pooled"])
+def test_prepared_decode_step_equals_one_shot_calls(pooled):
+    """A DecodeStep bound to fixed buffers, refilled with new inputs every step, gives
+    bit for bit what the one-shot call gives on the same inputs (plain and pooled)."""
+    P, N, H, K = 12, 5, 3, 6
+    S_init = up(make_decode_state(P if pooled else N, H, 128, seed=31))
+    slots = torch.tensor([7, 0, 11, 3, 5], dtype=torch.int32, device=dev()) if pooled else None
+    bufs = {n: None for n in ("q", "k", "v", "g", "beta")}
+    first = make_decode_step(N, H, 128, seed=31, step=0)
+    for n in bufs:
+        bufs[n] = up(getattr(first, n)).clone()
+    S_a, S_b = S_init.clone(), S_init.clone()
+    o_a = torch.empty((N, H, 128), device=dev())
+    o_b = torch.empty((N, H, 128), device=dev())
+    step = kda.DecodeStep(*(bufs[n] for n in ("q", "k", "v", "g", "beta")), S_a, o=o_a, slots=slots)
+    for s in range(K):
+        st = make_decode_step(N, H, 128, seed=31, step=s)
+        for n in bufs:                                     # refill the bound buffers
+            bufs[n].copy_(up(getattr(st, n)))
+        step()
+        args = [up(getattr(st, n)) for n in ("q", "k", "v", "g", "beta")]
+        if pooled:
+            kda.kda_decode_step_pooled(*args, S_b, slots, o=o_b)
+        else:
+            kda.kda_decode_step(*args, S_b, o=o_b)
+        torch.cuda.synchronize()
+        assert torch.equal(o_a, o_b), ("step", s)
+    assert torch.equal(S_a, S_b)
