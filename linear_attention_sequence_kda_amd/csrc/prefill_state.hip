@@ -769,7 +769,9 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
 // column blocks of a chain share an XCD (ids equal modulo 8), so each map is fetched
 // from memory once into that XCD's L2.  The next map's rows are loaded while the
 // current product runs; each 16x16 result tile accumulates in four independent chains
-// over the 128-long contraction.
+// over the 128-long contraction.  The contraction index of MFMA k-slot s (lane group
+// s = lane / 16) at step q4, element e is 16 q4 + 4 s + e, so the four lanes of a map
+// row read 64 contiguous bytes per load.
 // ---------------------------------------------------------------------------
 struct MapRows {
   float4 a[2][8];     // A rows (2 tiles), contraction 32lg .. 32lg + 31
@@ -815,9 +817,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void map_chain(ChainArgs a) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int row0 = (2 * wave + it) * 16;
-      const float *arow = A + (size_t)(row0 + lr) * (2 * D) + 32 * lg;
+      const float *arow = A + (size_t)(row0 + lr) * (2 * D) + 4 * lg;
 #pragma unroll
-      for (int q4 = 0; q4 < 8; ++q4) m.a[it][q4] = *reinterpret_cast<const float4 *>(arow + 4 * q4);
+      for (int q4 = 0; q4 < 8; ++q4) m.a[it][q4] = *reinterpret_cast<const float4 *>(arow + 16 * q4);
 #pragma unroll
       for (int r = 0; r < 4; ++r) m.b[it][r] = add_b ? A[(size_t)(row0 + 4 * lg + r) * (2 * D) + bcol + lr] : 0.f;
     }
@@ -827,11 +829,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void map_chain(ChainArgs a) {
   // next one.
   MapRows m0, m1;
   if (steps > 0) load_map(m0, 0);                      // in flight while the first block loads
-  for (int x = tid; x < 16 * D; x += NTHREADS) {
-    const int i = x / 16, n = x % 16;
-    const float v = x0 ? x0[(size_t)i * a.x0_ld + n] : 0.f;
-    sXt[0][n][i] = v;
-    if (a.store_x0) out0[(size_t)i * a.out_ld + n] = v;
+  // all loads of the first block before any store: written as one loop, the compiler
+  // waited for each load before the next (x0 and out may alias as far as it knows)
+  constexpr int XPT = 16 * D / NTHREADS;
+  float xv[XPT];
+#pragma unroll
+  for (int u = 0; u < XPT; ++u) {
+    const int x = tid + u * NTHREADS, i = x / 16, n = x % 16;
+    xv[u] = x0 ? x0[(size_t)i * a.x0_ld + n] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < XPT; ++u) {
+    const int x = tid + u * NTHREADS, i = x / 16, n = x % 16;
+    sXt[0][n][i] = xv[u];
+    if (a.store_x0) out0[(size_t)i * a.out_ld + n] = xv[u];
   }
   if (steps <= 0) return;                              // the whole workgroup leaves
   __syncthreads();
@@ -839,6 +850,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void map_chain(ChainArgs a) {
     // unconditional (the last step reloads the last map), so that the compiler's waits
     // for cur count exactly the loads issued after it
     load_map(nxt, min(j + 1, steps - 1));
+    asm volatile("" ::: "memory");                     // keeps those loads ahead of the products
     f32x4 res[2];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -846,7 +858,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void map_chain(ChainArgs a) {
 #pragma unroll
       for (int q4 = 0; q4 < 8; ++q4) {
         const float4 av = cur.a[it][q4];
-        const float4 bv = *reinterpret_cast<const float4 *>(&sXt[j & 1][lr][32 * lg + 4 * q4]);
+        const float4 bv = *reinterpret_cast<const float4 *>(&sXt[j & 1][lr][16 * q4 + 4 * lg]);
         c[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, c[0], 0, 0, 0);
         c[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, c[1], 0, 0, 0);
         c[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, c[2], 0, 0, 0);
