@@ -765,17 +765,18 @@ __global__ __launch_bounds__((Shape<NC, MODE>::NTH), 1) void chunk_state_kernel(
 //   3. within:   S_in at every other segment, one chain per group from its first state
 // and from one launch of the third kind over a single group for smaller n.
 //
-// One workgroup per (chain, 16-column block); the map product runs as fp32 MFMA.  The
-// column blocks of a chain share an XCD (ids equal modulo 8), so each map is fetched
-// from memory once into that XCD's L2.  The next map's rows are loaded while the
+// One workgroup per (chain, one or two 16-column blocks); the map product runs as fp32
+// MFMA.  The workgroups of a chain share an XCD (ids equal modulo 8), so each map is
+// fetched from memory once into that XCD's L2.  The next map's rows are loaded while the
 // current product runs; each 16x16 result tile accumulates in four independent chains
 // over the 128-long contraction.  The contraction index of MFMA k-slot s (lane group
 // s = lane / 16) at step q4, element e is 16 q4 + 4 s + e, so the four lanes of a map
 // row read 64 contiguous bytes per load.
 // ---------------------------------------------------------------------------
+template <int NB>
 struct MapRows {
-  float4 a[2][8];     // A rows (2 tiles), contraction 32lg .. 32lg + 31
-  float b[2][4];      // B at rows 4lg + r of each tile, this lane's column
+  float4 a[2][8];     // A rows (2 tiles), contraction 16 q4 + 4 lg + (0..3)
+  float b[NB][2][4];  // B at rows 4lg + r of each tile, this lane's column of each block
 };
 
 struct ChainArgs {
@@ -794,14 +795,18 @@ struct ChainArgs {
   int store_x0, store_all;      // store the first block too (at the chain's output base)
 };
 
+// NB: 16-column blocks per workgroup (the A rows a wave loads serve all of them)
 // (no __restrict__ on the maps: with it the compiler sinks the prefetch loads of the
 // next map to their uses, exposing their latency at every step)
+template <int NB>
 __global__ __launch_bounds__(NTHREADS, 1) void map_chain(ChainArgs a) {
-  __shared__ __align__(16) float sXt[2][16][D + 4];   // the block, transposed [n][i], double buffered
+  constexpr int NCOL = 16 * NB;
+  __shared__ __align__(16) float sXt[2][NCOL][D + 4];   // the block, transposed [n][i], double buffered
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lr = lane & 15, lg = lane >> 4;
   const int xcd = blockIdx.x & 7, rest = blockIdx.x >> 3;
-  const int cb = rest % a.ncb, chain = (rest / a.ncb) * 8 + xcd;
+  const int nwg = a.ncb / NB;                          // workgroups per chain
+  const int cb = (rest % nwg) * NB, chain = (rest / nwg) * 8 + xcd;
   if (chain >= a.n_bh * a.n_grp) return;
   const int bh = chain / a.n_grp, g = chain % a.n_grp;
   const int steps = min(a.grp_len, a.n_total - g * a.grp_len) - 1;
@@ -812,7 +817,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void map_chain(ChainArgs a) {
   const float *x0 = a.x0 ? a.x0 + bh * a.x0_bh + g * a.x0_grp + c0 : nullptr;
   float *out0 = a.out + bh * a.out_bh + g * a.out_grp + c0;
   // wave w computes rows 32w .. 32w + 31 (two 16-row tiles)
-  auto load_map = [&](MapRows &m, int j) __attribute__((always_inline)) {
+  auto load_map = [&](MapRows<NB> &m, int j) __attribute__((always_inline)) {
     const float *A = map0 + (size_t)j * D * (2 * D);
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -821,62 +826,75 @@ __global__ __launch_bounds__(NTHREADS, 1) void map_chain(ChainArgs a) {
 #pragma unroll
       for (int q4 = 0; q4 < 8; ++q4) m.a[it][q4] = *reinterpret_cast<const float4 *>(arow + 16 * q4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) m.b[it][r] = add_b ? A[(size_t)(row0 + 4 * lg + r) * (2 * D) + bcol + lr] : 0.f;
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          m.b[nb][it][r] = add_b ? A[(size_t)(row0 + 4 * lg + r) * (2 * D) + bcol + 16 * nb + lr] : 0.f;
     }
   };
   // Two map buffers in fixed roles per half of the unrolled loop (no register copies
   // between them), so that the waits for one map's rows do not cover the loads of the
   // next one.
-  MapRows m0, m1;
+  MapRows<NB> m0, m1;
   if (steps > 0) load_map(m0, 0);                      // in flight while the first block loads
   // all loads of the first block before any store: written as one loop, the compiler
   // waited for each load before the next (x0 and out may alias as far as it knows)
-  constexpr int XPT = 16 * D / NTHREADS;
+  constexpr int XPT = NCOL * D / NTHREADS;
   float xv[XPT];
 #pragma unroll
   for (int u = 0; u < XPT; ++u) {
-    const int x = tid + u * NTHREADS, i = x / 16, n = x % 16;
+    const int x = tid + u * NTHREADS, i = x / NCOL, n = x % NCOL;
     xv[u] = x0 ? x0[(size_t)i * a.x0_ld + n] : 0.f;
   }
 #pragma unroll
   for (int u = 0; u < XPT; ++u) {
-    const int x = tid + u * NTHREADS, i = x / 16, n = x % 16;
+    const int x = tid + u * NTHREADS, i = x / NCOL, n = x % NCOL;
     sXt[0][n][i] = xv[u];
     if (a.store_x0) out0[(size_t)i * a.out_ld + n] = xv[u];
   }
   if (steps <= 0) return;                              // the whole workgroup leaves
   __syncthreads();
-  auto step = [&](MapRows &cur, MapRows &nxt, int j) __attribute__((always_inline)) {
+  auto step = [&](MapRows<NB> &cur, MapRows<NB> &nxt, int j) __attribute__((always_inline)) {
     // unconditional (the last step reloads the last map), so that the compiler's waits
     // for cur count exactly the loads issued after it
     load_map(nxt, min(j + 1, steps - 1));
     asm volatile("" ::: "memory");                     // keeps those loads ahead of the products
-    f32x4 res[2];
+    f32x4 res[NB][2];
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-      f32x4 c[4] = {zero4(), zero4(), zero4(), zero4()};
+      f32x4 c[NB][4];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) c[nb][0] = c[nb][1] = c[nb][2] = c[nb][3] = zero4();
 #pragma unroll
       for (int q4 = 0; q4 < 8; ++q4) {
         const float4 av = cur.a[it][q4];
-        const float4 bv = *reinterpret_cast<const float4 *>(&sXt[j & 1][lr][16 * q4 + 4 * lg]);
-        c[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, c[0], 0, 0, 0);
-        c[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, c[1], 0, 0, 0);
-        c[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, c[2], 0, 0, 0);
-        c[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, c[3], 0, 0, 0);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          const float4 bv = *reinterpret_cast<const float4 *>(&sXt[j & 1][16 * nb + lr][16 * q4 + 4 * lg]);
+          c[nb][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.x, bv.x, c[nb][0], 0, 0, 0);
+          c[nb][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.y, bv.y, c[nb][1], 0, 0, 0);
+          c[nb][2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.z, bv.z, c[nb][2], 0, 0, 0);
+          c[nb][3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av.w, bv.w, c[nb][3], 0, 0, 0);
+        }
       }
 #pragma unroll
-      for (int r = 0; r < 4; ++r) res[it][r] = ((c[0][r] + c[1][r]) + (c[2][r] + c[3][r])) + cur.b[it][r];
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          res[nb][it][r] = ((c[nb][0][r] + c[nb][1][r]) + (c[nb][2][r] + c[nb][3][r])) + cur.b[nb][it][r];
     }
     const bool st = a.store_all || j == steps - 1;
     float *dst = out0 + (a.store_all ? (j + 1) * a.out_step : 0);
 #pragma unroll
-    for (int it = 0; it < 2; ++it)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = (2 * wave + it) * 16 + 4 * lg + r;
-        sXt[(j + 1) & 1][lr][i] = res[it][r];   // the other buffer: no wait for readers of this one
-        if (st) dst[(size_t)i * a.out_ld + lr] = res[it][r];
-      }
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = (2 * wave + it) * 16 + 4 * lg + r;
+          sXt[(j + 1) & 1][16 * nb + lr][i] = res[nb][it][r];   // the other buffer: no wait for readers of this one
+          if (st) dst[(size_t)i * a.out_ld + 16 * nb + lr] = res[nb][it][r];
+        }
     // the new block visible to all waves; a barrier without a memory fence, so that the
     // global stores of the block are not waited for
     asm volatile("" ::: "memory");
@@ -890,10 +908,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void map_chain(ChainArgs a) {
   }
 }
 
+// Two column blocks per workgroup halve the map rows read per step (the A rows serve
+// both), at one workgroup per CU; worth it while that still gives every CU a workgroup.
 hipError_t launch_chain(const ChainArgs &a, hipStream_t s) {
   const int64_t chains = (int64_t)a.n_bh * a.n_grp;
-  const unsigned grid = static_cast<unsigned>((chains + 7) / 8 * 8 * a.ncb);
-  hipLaunchKernelGGL(map_chain, dim3(grid), dim3(NTHREADS), 0, s, a);
+  const int64_t slots = (chains + 7) / 8 * 8;
+  if (slots * (a.ncb / 2) >= 256) {
+    hipLaunchKernelGGL(map_chain<2>, dim3(static_cast<unsigned>(slots * (a.ncb / 2))), dim3(NTHREADS), 0, s, a);
+  } else {
+    hipLaunchKernelGGL(map_chain<1>, dim3(static_cast<unsigned>(slots * a.ncb)), dim3(NTHREADS), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -333,3 +333,14 @@ def test_scale_returns_to_one():
 def test_segments_grouped_scan(T, n_seg):
     c = make_prefill(1, T, 2, 128, seed=57 + n_seg, in_dtype=BF16, s0_std=0.05)
     check(c, f"grouped scan, {n_seg} segments", chunk=64, n_segments=n_seg, ckpt_every=256)
+
+
+@pytest.mark.parametrize("H,T,n_seg", [(60, 640, 3), (12, 2560, 40)])
+def test_scan_two_column_blocks(H, T, n_seg):
+    """Enough chains for the scan to give each workgroup two 16-column blocks: 60 heads in
+    one chain each (padded to 64 chains, the padding exits at once), and 12 heads over 40
+    segments, whose compose and within-group launches take two blocks and whose launch over
+    the 12 group chains takes one."""
+    c = make_prefill(1, T, H, 128, seed=71 + n_seg, in_dtype=BF16, s0_std=0.05)
+    check(c, f"scan with two column blocks per workgroup, {H} heads, {n_seg} segments", chunk=64,
+          n_segments=n_seg)
