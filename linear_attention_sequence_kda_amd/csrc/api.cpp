@@ -47,7 +47,6 @@ bool valid_dtype(int32_t dt) { return dt == KDA_F32 || dt == KDA_BF16; }
 // ---------------------------------------------------------------------------
 // prefill planning
 // ---------------------------------------------------------------------------
-constexpr int kTargetWorkgroups = 256;   // one per CU of MI355X
 
 kda_status plan_prefill(const kda_prefill_desc &d, PrefillPlan *p) {
   std::memset(p, 0, sizeof(*p));
@@ -66,7 +65,7 @@ kda_status plan_prefill(const kda_prefill_desc &d, PrefillPlan *p) {
   if (ns > 1 && ns > n_chunks) return KDA_ERR_SHAPE;
   if (ns == 0) {
     ns = 1;
-    while (units * vs * ns < kTargetWorkgroups && n_chunks / (ns * 2) >= 8) ns *= 2;
+    while (units * vs * ns < kda::kCUs && n_chunks / (ns * 2) >= 8) ns *= 2;
   }
   if (ns < 1) ns = 1;
   int64_t seg_chunks = n_chunks > 0 ? (n_chunks + ns - 1) / ns : 0;

@@ -9,6 +9,8 @@
 
 namespace kda {
 
+constexpr int kCUs = 256;   // compute units of MI355X: launches aim at one workgroup per CU
+
 // slots: null for the plain form (state [N, H, d_k, d_v]); else the pool slot of each
 // sequence (state [pool, H, d_k, d_v]).
 hipError_t launch_decode(const kda_decode_desc &d, const int32_t *slots, int32_t pool, hipStream_t s);
