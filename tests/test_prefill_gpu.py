@@ -335,12 +335,12 @@ def test_segments_grouped_scan(T, n_seg):
     check(c, f"grouped scan, {n_seg} segments", chunk=64, n_segments=n_seg, ckpt_every=256)
 
 
-@pytest.mark.parametrize("H,T,n_seg", [(60, 640, 3), (12, 2560, 40)])
-def test_scan_two_column_blocks(H, T, n_seg):
+@pytest.mark.parametrize("H,T,n_seg,s0", [(60, 640, 3, True), (64, 512, 2, False), (12, 2560, 40, True)])
+def test_scan_two_column_blocks(H, T, n_seg, s0):
     """Enough chains for the scan to give each workgroup two 16-column blocks: 60 heads in
-    one chain each (padded to 64 chains, the padding exits at once), and 12 heads over 40
-    segments, whose compose and within-group launches take two blocks and whose launch over
-    the 12 group chains takes one."""
+    one chain each (padded to 64 chains, the padding exits at once); 64 heads from a zero
+    initial state; and 12 heads over 40 segments, whose compose and within-group launches
+    take two blocks and whose launch over the 12 group chains takes one."""
     c = make_prefill(1, T, H, 128, seed=71 + n_seg, in_dtype=BF16, s0_std=0.05)
-    check(c, f"scan with two column blocks per workgroup, {H} heads, {n_seg} segments", chunk=64,
-          n_segments=n_seg)
+    check(c, f"scan with two column blocks per workgroup, {H} heads, {n_seg} segments, S0={s0}",
+          chunk=64, n_segments=n_seg, S0=s0)
