@@ -38,6 +38,7 @@ struct PrepArgs {
   unsigned char *rec;     // n_recs records of Rec<C, F32>::bytes
   int T, H, n_chunks;
   int64_t n_recs;         // B * H * n_chunks
+  int chunk_major;        // workgroup order: all heads of a chunk, then the next chunk
 };
 
 template <int C, bool F32>
@@ -195,8 +196,12 @@ __global__ __launch_bounds__(NTHREADS, F32 ? 1 : (C == 64 ? 4 : 2)) void chunk_p
     for (int x = tid; x < (KC - C) * D; x += NTHREADS) { sKT[C * D + x] = T(0); sKF[C * D + x] = T(0); }
   }
 
-  const int64_t rec = blockIdx.x;
-  if (rec >= a.n_recs) return;
+  if ((int64_t)blockIdx.x >= a.n_recs) return;
+  int64_t rec = blockIdx.x;                            // records stay [B * H][n_chunks]
+  if (a.chunk_major) {
+    const int64_t n_bh = a.n_recs / a.n_chunks;
+    rec = ((int64_t)blockIdx.x % n_bh) * a.n_chunks + (int64_t)blockIdx.x / n_bh;
+  }
   RawPrep<F32> raw;
   load_prep<C, F32>(raw, a, rec, tid);
   {
@@ -552,6 +557,12 @@ hipError_t launch_prefill_prep(const kda_prefill_desc &d, int n_chunks, void *re
   a.T = d.T; a.H = d.H; a.n_chunks = n_chunks;
   a.n_recs = (int64_t)d.B * d.H * n_chunks;
   if (a.n_recs == 0) return hipSuccess;
+  // The workgroups resident at one time (four per CU) are consecutive ids.  In head-major
+  // order, with 1024 or more chunks per head they all read one head: 256 bytes of every
+  // token row of q, k and g.  Chunk-major order then makes them read whole token rows
+  // (131k workload: prep 829 -> 778 us).  With fewer chunks head-major order already
+  // spans several heads and measured slightly faster for the passes after it.
+  a.chunk_major = n_chunks >= 4 * kCUs;
   if (d.in_dtype == KDA_F32) return launch_prep_t<16, true>(a, s);
   if (d.chunk == 16) return launch_prep_t<16, false>(a, s);
   return launch_prep_t<64, false>(a, s);

@@ -335,6 +335,16 @@ def test_segments_grouped_scan(T, n_seg):
     check(c, f"grouped scan, {n_seg} segments", chunk=64, n_segments=n_seg, ckpt_every=256)
 
 
+# ---------------------------------------------------------------------------
+# 1024 or more chunks per head: the prep kernel takes its workgroups chunk-major (every
+# head of a chunk, then the next chunk); records keep their head-major layout
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("B,H,T,chunk", [(2, 3, 16384, 16), (1, 2, 64 * 1024 + 37, 64)])
+def test_prep_chunk_major_order(B, H, T, chunk):
+    c = make_prefill(B, T, H, 128, seed=83 + chunk, in_dtype=BF16, s0_std=0.05)
+    check(c, f"chunk-major prep, B={B} H={H} T={T} chunk={chunk}", chunk=chunk)
+
+
 @pytest.mark.parametrize("H,T,n_seg,s0", [(60, 640, 3, True), (64, 512, 2, False), (12, 2560, 40, True)])
 def test_scan_two_column_blocks(H, T, n_seg, s0):
     """Enough chains for the scan to give each workgroup two 16-column blocks: 60 heads in
